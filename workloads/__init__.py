@@ -1,0 +1,184 @@
+"""Seeded synthetic inputs shaped like video-VAE decoder workloads.
+
+This module only draws random numbers and names shapes.  It holds none of the
+convolution or normalisation arithmetic, so both the HIP path and the oracle
+may use it without sharing any of the method.
+
+Recipe (one numpy PCG64 stream per tensor):
+  * workload k uses ``numpy.random.SeedSequence(1000 + k)``, spawned into one
+    child per tensor in a fixed order (x, then per layer gamma, beta, w, b);
+  * activations ~ N(0, 1), drawn as float32 and rounded once to fp16 (RNE);
+  * weights ~ U(-a, a) drawn in float64, rounded once to fp16, with
+    a = 1/sqrt(27*Cin) for the small zero-padded workload and the
+    Kaiming-uniform bound a = sqrt(6 / fan_in), fan_in = kt*kh*kw*Cin, elsewhere;
+  * biases ~ N(0, 0.1) for the small workload and N(0, 0.02) elsewhere;
+  * GroupNorm gamma ~ N(1, 0.1), beta ~ N(0, 0.1);
+  * the channel-changing workload scales round(1% of Cin) = 5 of 512 input
+    channels, picked by a seeded permutation, by 50 before the fp16 cast.
+
+Layouts: activations NDHWC [N, T, H, W, C]; weights [Cout, kt, kh, kw, Cin].
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+TPAD_ZERO = 0
+TPAD_REPLICATE = 1
+
+
+@dataclass(frozen=True)
+class ConvShape:
+    """Input-side description of one stride-1 conv3d (padding is given, not derived)."""
+    n: int
+    t: int
+    h: int
+    w: int
+    cin: int
+    cout: int
+    kt: int = 3
+    kh: int = 3
+    kw: int = 3
+    pad_t_front: int = 2
+    pad_t_back: int = 0
+    pad_h: int = 1
+    pad_w: int = 1
+    tmode: int = TPAD_REPLICATE
+
+    @property
+    def pads(self):
+        return (self.pad_t_front, self.pad_t_back, self.pad_h, self.pad_w)
+
+    @property
+    def x_shape(self):
+        return (self.n, self.t, self.h, self.w, self.cin)
+
+    @property
+    def w_shape(self):
+        return (self.cout, self.kt, self.kh, self.kw, self.cin)
+
+
+# The five workloads.  Index k below is the workload number used for seeding.
+SMALL_ZERO = ConvShape(1, 5, 16, 16, 32, 32, pad_t_front=1, pad_t_back=1, tmode=TPAD_ZERO)
+CAUSAL_512 = ConvShape(1, 9, 64, 64, 512, 512)
+CAUSAL_256 = ConvShape(1, 17, 128, 128, 256, 256)
+CAUSAL_256_T1 = replace(CAUSAL_256, t=1)
+STAGE_3X3 = ConvShape(1, 33, 256, 256, 512, 256)
+STAGE_1X1 = ConvShape(1, 33, 256, 256, 256, 128, kt=1, kh=1, kw=1, pad_t_front=0, pad_t_back=0,
+                      pad_h=0, pad_w=0, tmode=TPAD_ZERO)
+BLOCK_CONV = ConvShape(1, 17, 128, 128, 256, 256)
+BLOCK_GROUPS = 32
+BLOCK_EPS = 1e-6
+
+WORKLOADS = {
+    0: "conv3d 3x3x3 zero-pad, N=1 T=5 H=W=16 Cin=Cout=32",
+    1: "causal conv3d 3x3x3, N=1 T=9 H=W=64 Cin=Cout=512",
+    2: "causal conv3d 3x3x3, N=1 T=17 H=W=128 Cin=Cout=256 (and T=1)",
+    3: "causal conv3d 3x3x3 512->256 + conv3d 1x1x1 256->128, N=1 T=33 H=W=256",
+    4: "3D ResNet decoder block GN(32)+SiLU -> causal conv -> GN+SiLU -> causal conv -> +x, "
+       "N=1 C=256 T=17 H=W=128",
+}
+
+
+def kaiming_bound(shape: ConvShape) -> float:
+    return float(np.sqrt(6.0 / (shape.kt * shape.kh * shape.kw * shape.cin)))
+
+
+def _rngs(seed: int, count: int):
+    return [np.random.Generator(np.random.PCG64(s))
+            for s in np.random.SeedSequence(seed).spawn(count)]
+
+
+def normal_f16(rng, shape, mean=0.0, std=1.0, chunk_elems=1 << 26):
+    """N(mean, std) drawn as float32 in sequential chunks, rounded once to fp16."""
+    out = np.empty(shape, np.float16)
+    flat = out.reshape(-1)
+    for s in range(0, flat.size, chunk_elems):
+        e = min(flat.size, s + chunk_elems)
+        v = rng.standard_normal(e - s, dtype=np.float32)
+        if std != 1.0:
+            v *= np.float32(std)
+        if mean != 0.0:
+            v += np.float32(mean)
+        flat[s:e] = v.astype(np.float16)
+    return out
+
+
+def uniform_f16(rng, shape, bound):
+    return rng.uniform(-bound, bound, size=shape).astype(np.float16)
+
+
+def conv_inputs(shape: ConvShape, seed: int, w_bound=None, b_std=0.02, with_bias=True,
+                hot_channels=0, hot_scale=50.0):
+    """x, w, b (fp16 numpy) for one conv.  ``hot_channels`` input channels x hot_scale."""
+    rx, rw, rb, rp = _rngs(seed, 4)
+    if w_bound is None:
+        w_bound = kaiming_bound(shape)
+    if hot_channels:
+        x = np.empty(shape.x_shape, np.float16)
+        hot = rp.permutation(shape.cin)[:hot_channels]
+        scale = np.ones(shape.cin, np.float32)
+        scale[hot] = np.float32(hot_scale)
+        xf = x.reshape(-1, shape.cin)
+        rows = xf.shape[0]
+        step = max(1, (1 << 25) // shape.cin)
+        for s in range(0, rows, step):
+            e = min(rows, s + step)
+            v = rx.standard_normal((e - s, shape.cin), dtype=np.float32)
+            v *= scale
+            xf[s:e] = v.astype(np.float16)
+    else:
+        x = normal_f16(rx, shape.x_shape)
+    w = uniform_f16(rw, shape.w_shape, w_bound)
+    b = normal_f16(rb, (shape.cout,), 0.0, b_std) if with_bias else None
+    return {"x": x, "w": w, "b": b}
+
+
+def workload_inputs(k: int):
+    """Inputs of workload k (0..4) as fp16 numpy arrays, seeded SeedSequence(1000+k)."""
+    seed = 1000 + k
+    if k == 0:
+        s = SMALL_ZERO
+        return dict(shape=s, **conv_inputs(s, seed, w_bound=1.0 / np.sqrt(27 * s.cin), b_std=0.1))
+    if k == 1:
+        return dict(shape=CAUSAL_512, **conv_inputs(CAUSAL_512, seed))
+    if k == 2:
+        return dict(shape=CAUSAL_256, **conv_inputs(CAUSAL_256, seed))
+    if k == 3:
+        a, b2 = np.random.SeedSequence(seed).spawn(2)
+        st1 = conv_inputs(STAGE_3X3, int(a.generate_state(1)[0]), hot_channels=5)
+        st2 = conv_inputs(STAGE_1X1, int(b2.generate_state(1)[0]))
+        return {"shape": STAGE_3X3, "x": st1["x"], "w": st1["w"], "b": st1["b"],
+                "shape2": STAGE_1X1, "w2": st2["w"], "b2": st2["b"]}
+    if k == 4:
+        return block_inputs(BLOCK_CONV, seed)
+    raise KeyError(k)
+
+
+def block_inputs(shape: ConvShape, seed: int):
+    """Decoder-block tensors in the order x, gamma1, beta1, w1, b1, gamma2, beta2, w2, b2."""
+    r = _rngs(seed, 9)
+    c = shape.cin
+    bound = kaiming_bound(shape)
+    return {
+        "shape": shape,
+        "x": normal_f16(r[0], shape.x_shape),
+        "gamma1": normal_f16(r[1], (c,), 1.0, 0.1),
+        "beta1": normal_f16(r[2], (c,), 0.0, 0.1),
+        "w1": uniform_f16(r[3], shape.w_shape, bound),
+        "b1": normal_f16(r[4], (shape.cout,), 0.0, 0.02),
+        "gamma2": normal_f16(r[5], (c,), 1.0, 0.1),
+        "beta2": normal_f16(r[6], (c,), 0.0, 0.1),
+        "w2": uniform_f16(r[7], shape.w_shape, bound),
+        "b2": normal_f16(r[8], (shape.cout,), 0.0, 0.02),
+        "groups": BLOCK_GROUPS,
+        "eps": BLOCK_EPS,
+    }
+
+
+def gn_inputs(n: int, thw_shape, c: int, seed: int, mean=0.0, std=1.0):
+    """x [n, *thw_shape, c], gamma ~ N(1, 0.1), beta ~ N(0, 0.1), all fp16."""
+    rx, rg, rb = _rngs(seed, 3)
+    x = normal_f16(rx, (n,) + tuple(thw_shape) + (c,), mean, std)
+    return {"x": x, "gamma": normal_f16(rg, (c,), 1.0, 0.1), "beta": normal_f16(rb, (c,), 0.0, 0.1)}
