@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark of the fp16 implicit-GEMM conv3d on one MI355X.
+
+One step = one conv3d_forward of the causal 3x3x3 conv, N=1, T=9, H=W=64,
+Cin=Cout=512, fp16 NDHWC, bias, inputs resident in HBM.  Prints ONE JSON line:
+value = conv TFLOP/s (2*M*Cout*K / time), a roofline object for the conv
+kernel (HIP events on its launch stream), the oracle timed on a bounded
+sample of the same workload on the host cores (cpu_baseline), the 3D ResNet
+decoder-block time in ms (GN+SiLU, causal conv, GN+SiLU, causal conv + x;
+N=1, C=256, T=17, 128x128), and per-kernel figures of the other hot-path
+kernels under "kernels".
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-seconds S]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("conv3d_igemm.hip", "c3d_internal.h"):
+        with open(os.path.join(ROOT, "convolution_implicit_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel, src_hash):
+    """HBM bytes per launch from the committed counter summary, if it matches this source."""
+    path = os.path.join(ROOT, "profiles", "conv3d_causal512_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    m_ker = re.search(r"kernel:\s*(\S+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_src and m_ker and m_b) or m_src.group(1) != src_hash or m_ker.group(1) != kernel:
+        return None
+    return float(m_b.group(1))
+
+
+def time_steps(fn, steps, warmup, torch):
+    """Wall time of `steps` calls between device syncs, and per-call HIP-event times (ms)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]
+    return wall * 1e3 / steps, per
+
+
+def desc_of(c3d, s, flags):
+    return c3d.make_desc(s.n, s.t, s.h, s.w, s.cin, s.cout, s.kt, s.kh, s.kw, s.pad_t_front,
+                         s.pad_t_back, s.pad_h, s.pad_w, s.tmode, flags)
+
+
+def out_dims(s):
+    return (s.n, s.t + s.pad_t_front + s.pad_t_back - s.kt + 1, s.h + 2 * s.pad_h - s.kh + 1,
+            s.w + 2 * s.pad_w - s.kw + 1, s.cout)
+
+
+def cpu_baseline_leg(d, y_dev, info, target_s, np):
+    """Time the fp64 oracle on a bounded sample of the workload; check the GPU there too."""
+    import oracle
+    s = d["shape"]
+    x64 = d["x"].astype(np.float64)
+    w64 = d["w"].astype(np.float64)
+    b64 = d["b"].astype(np.float64)
+    k = s.kt * s.kh * s.kw * s.cin
+    rng = np.random.default_rng(2024)
+    m_total = int(info.gemm_m)
+
+    def run(nvox):
+        m = np.repeat(np.sort(rng.choice(m_total, nvox, replace=False)), s.cout)
+        co = np.tile(np.arange(s.cout), nvox)
+        t0 = time.perf_counter()
+        ref, mag = oracle.conv3d_points(x64, w64, b64, None, s.pads, s.tmode, m, co)
+        return time.perf_counter() - t0, m, co, ref, mag
+
+    dt, *_ = run(8)
+    per_vox = max(dt / 8, 1e-6)
+    nvox = int(min(m_total, max(16, target_s / per_vox)))
+    dt, m, co, ref, mag = run(nvox)
+    flops = 2.0 * k * m.size
+    got = y_dev.reshape(-1, s.cout)[m, co].astype(np.float64)
+    a = np.abs(ref)
+    ulp = np.exp2(np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -14) - 10)
+    ok = bool(np.all(np.abs(got - ref) <= 2e-3 * mag + ulp))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d output voxels x all %d channels (%.3g GFLOP of %.3g), fp64 "
+                      "seven-loop oracle, %.1f s wall" % (nvox, s.cout, flops / 1e9,
+                                                          info.flops / 1e9, dt),
+            "seconds": dt, "gpu_matches_oracle_on_sample": ok}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall seconds of oracle work for cpu_baseline (0 disables it)")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel extras")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import convolution_implicit_gemm_amd as c3d
+    import workloads
+
+    c3d.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def T(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---- headline: causal conv3d 3x3x3, 512 -> 512, T=9, 64x64
+    log("generating the causal 512-channel workload")
+    d1 = workloads.workload_inputs(1)
+    s1 = d1["shape"]
+    plan = c3d.conv3d_plan(desc_of(c3d, s1, c3d.CONV3D_F_BIAS))
+    info = plan.info()
+    x, w, b = T(d1["x"]), T(d1["w"]), T(d1["b"])
+    y = torch.empty(out_dims(s1), dtype=torch.float16, device=dev)
+
+    def step():
+        c3d.conv3d_forward(plan, x, w, b, None, y)
+
+    log("timing %d steps after %d warmup" % (args.steps, args.warmup))
+    ms, per = time_steps(step, args.steps, args.warmup, torch)
+    kernel_ms = sum(per) / len(per)
+    value = info.flops / (ms * 1e-3) / 1e12
+    achieved = info.flops / (kernel_ms * 1e-3) / 1e12
+    kname = info.kernel_name.decode()
+    src_hash = kernel_source_hash()
+    result = {
+        "metric": "fp16 conv3d 3x3x3 TFLOP/s on 1 MI355X (% of fp16 MFMA peak); decoder-block ms",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic (seeded N(0,1) activations, Kaiming-uniform fp16 weights)",
+        "config": {"workload": "causal conv3d 3x3x3 (first frame replicated twice in front, "
+                               "spatial zero pad 1), N=1 T=9 H=W=64 Cin=Cout=512, fp16 NDHWC",
+                   "gemm_m": int(info.gemm_m), "gemm_n": int(info.gemm_n),
+                   "gemm_k": int(info.gemm_k), "kernel": kname, "grid": int(info.grid),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                     "traffic": committed_traffic(kname, src_hash),
+                     "kernel_ms": round(kernel_ms, 4), "source_sha256_16": src_hash},
+    }
+
+    # ---- decoder block: GN+SiLU -> causal conv -> GN+SiLU -> causal conv + x
+    log("decoder block")
+    d4 = workloads.workload_inputs(4)
+    s4 = d4["shape"]
+    thw = s4.t * s4.h * s4.w
+    bp1 = c3d.conv3d_plan(desc_of(c3d, s4, c3d.CONV3D_F_BIAS))
+    bp2 = c3d.conv3d_plan(desc_of(c3d, s4, c3d.CONV3D_F_BIAS | c3d.CONV3D_F_RESIDUAL))
+    gws = torch.zeros(c3d.groupnorm_silu_workspace(1, thw, s4.cin, 32), dtype=torch.uint8,
+                      device=dev)
+    bx = T(d4["x"])
+    bt = {k: T(d4[k]) for k in ("gamma1", "beta1", "w1", "b1", "gamma2", "beta2", "w2", "b2")}
+    a1, c1, a2, out = (torch.empty_like(bx) for _ in range(4))
+
+    def block():
+        c3d.groupnorm_silu(bx, bt["gamma1"], bt["beta1"], a1, 1, thw, s4.cin, 32, 1e-6, True, gws)
+        c3d.conv3d_forward(bp1, a1, bt["w1"], bt["b1"], None, c1)
+        c3d.groupnorm_silu(c1, bt["gamma2"], bt["beta2"], a2, 1, thw, s4.cout, 32, 1e-6, True, gws)
+        c3d.conv3d_forward(bp2, a2, bt["w2"], bt["b2"], bx, out)
+
+    bms, bper = time_steps(block, max(5, args.steps // 2), max(2, args.warmup), torch)
+    result["decoder_block_ms"] = round(sum(bper) / len(bper), 4)
+    result["decoder_block_config"] = ("GN(32, eps 1e-6)+SiLU -> causal conv3d 3x3x3 -> GN+SiLU -> "
+                                      "causal conv3d 3x3x3 -> +x; N=1 C=256 T=17 H=W=128 fp16")
+
+    if not args.no_kernels:
+        kern = {}
+        conv_flops = bp1.info().flops
+
+        def conv_only():
+            c3d.conv3d_forward(bp1, a1, bt["w1"], bt["b1"], None, c1)
+        _, p = time_steps(conv_only, 10, 2, torch)
+        t = sum(p) / len(p)
+        kern["causal_conv_256_T17"] = {"ms": round(t, 4), "TFLOP/s": round(conv_flops / t / 1e9, 1),
+                                       "kernel": bp1.info().kernel_name.decode()}
+
+        def gn_only():
+            c3d.groupnorm_silu(bx, bt["gamma1"], bt["beta1"], a1, 1, thw, s4.cin, 32, 1e-6, True,
+                               gws)
+        _, p = time_steps(gn_only, 10, 2, torch)
+        t = sum(p) / len(p)
+        sbytes = bx.numel() * 2
+        kern["groupnorm_silu_256_T17"] = {"ms": round(t, 4),
+                                          "GB/s_effective_2S": round(2 * sbytes / t / 1e6, 1),
+                                          "GB/s_as_implemented_3S": round(3 * sbytes / t / 1e6, 1)}
+
+        s1f = workloads.CAUSAL_256_T1
+        pt1 = c3d.conv3d_plan(desc_of(c3d, s1f, c3d.CONV3D_F_BIAS))
+        ws1 = torch.empty(pt1.workspace_bytes, dtype=torch.uint8, device=dev)
+        x1 = bx[:, :1].contiguous()
+        y1 = torch.empty(out_dims(s1f), dtype=torch.float16, device=dev)
+
+        def t1():
+            c3d.conv3d_forward(pt1, x1, bt["w1"], bt["b1"], None, y1, ws1)
+        _, p = time_steps(t1, 20, 3, torch)
+        t = sum(p) / len(p)
+        kern["first_frame_fold_256"] = {"us": round(t * 1e3, 2),
+                                        "TFLOP/s_folded": round(pt1.info().flops / t / 1e9, 1),
+                                        "path": int(pt1.info().path)}
+        del x1, y1, ws1, a1, c1, a2, out, bx
+
+        log("channel-changing stage (2.2 GB input)")
+        d3 = workloads.workload_inputs(3)
+        s3, s3b = d3["shape"], d3["shape2"]
+        p3 = c3d.conv3d_plan(desc_of(c3d, s3, c3d.CONV3D_F_BIAS))
+        p3b = c3d.conv3d_plan(desc_of(c3d, s3b, c3d.CONV3D_F_BIAS))
+        x3, w3, b3 = T(d3["x"]), T(d3["w"]), T(d3["b"])
+        del d3["x"]
+        y3 = torch.empty(out_dims(s3), dtype=torch.float16, device=dev)
+        w3b, b3b = T(d3["w2"]), T(d3["b2"])
+        y3b = torch.empty(out_dims(s3b), dtype=torch.float16, device=dev)
+
+        def st1():
+            c3d.conv3d_forward(p3, x3, w3, b3, None, y3)
+        _, p = time_steps(st1, 3, 1, torch)
+        t = sum(p) / len(p)
+        kern["causal_conv_512to256_T33_256x256"] = {"ms": round(t, 3),
+                                                    "TFLOP/s": round(p3.info().flops / t / 1e9, 1),
+                                                    "kernel": p3.info().kernel_name.decode()}
+
+        def st2():
+            c3d.conv3d_forward(p3b, y3, w3b, b3b, None, y3b)
+        _, p = time_steps(st2, 10, 2, torch)
+        t = sum(p) / len(p)
+        pw_bytes = y3.numel() * 2 + y3b.numel() * 2 + w3b.numel() * 2
+        kern["pointwise_256to128_T33_256x256"] = {"ms": round(t, 4),
+                                                  "GB/s": round(pw_bytes / t / 1e6, 1),
+                                                  "frac_of_hbm": round(pw_bytes / t / 1e6 / PEAK_HBM_GBS, 3),
+                                                  "kernel": p3b.info().kernel_name.decode()}
+        del x3, y3, y3b
+        result["kernels"] = kern
+
+    if args.cpu_seconds > 0:
+        log("cpu baseline: oracle on a bounded sample")
+        step()
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = cpu_baseline_leg(d1, y.cpu().numpy(), info, args.cpu_seconds, np)
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

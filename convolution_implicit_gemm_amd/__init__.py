@@ -1,0 +1,206 @@
+"""Python binding of libconv3d (MI355X / gfx950 fp16 implicit-GEMM conv3d).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libconv3d.so``.  The functions carry the C names of
+``include/conv3d.h``.  Tensor arguments may be torch tensors (their
+``data_ptr()`` is passed) or raw device addresses (ints); the stream defaults
+to torch's current stream on the current device.  There is no CPU fallback:
+if the library is missing, importing a function raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libconv3d.so")
+
+CONV3D_OK = 0
+CONV3D_ERR_INVALID_ARG = 1
+CONV3D_ERR_UNSUPPORTED = 2
+CONV3D_ERR_WORKSPACE = 3
+CONV3D_ERR_NO_DEVICE = 4
+CONV3D_ERR_HIP = 5
+
+CONV3D_TPAD_ZERO = 0
+CONV3D_TPAD_REPLICATE = 1
+
+CONV3D_F_BIAS = 1
+CONV3D_F_RESIDUAL = 2
+CONV3D_F_NO_T1_FASTPATH = 4
+
+CONV3D_PATH_GENERAL = 0
+CONV3D_PATH_T1_FOLD = 1
+CONV3D_PATH_POINTWISE = 2
+
+EXPORTED = ("conv3d_plan", "conv3d_plan_query", "conv3d_plan_destroy", "conv3d_forward",
+            "groupnorm_silu_workspace", "groupnorm_silu", "conv3d_status_str",
+            "conv3d_last_error", "conv3d_version")
+
+
+class conv3d_desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n", "t", "h", "w", "c_in", "c_out", "kt", "kh", "kw",
+                 "pad_t_front", "pad_t_back", "pad_h", "pad_w", "t_pad_mode")] + \
+               [("flags", ctypes.c_uint32)]
+
+
+class conv3d_plan_info(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("t_out", ctypes.c_int32), ("h_out", ctypes.c_int32),
+                ("w_out", ctypes.c_int32), ("gemm_m", ctypes.c_int64), ("gemm_n", ctypes.c_int64),
+                ("gemm_k", ctypes.c_int64), ("flops", ctypes.c_double), ("tile_m", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("grid", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t), ("kernel_name", ctypes.c_char * 64)]
+
+
+class Conv3dError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s (status %d): %s" % (_status_name(status), status, message))
+        self.status = status
+
+
+def _status_name(s):
+    return {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "NO_DEVICE",
+            5: "HIP"}.get(s, "UNKNOWN")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libconv3d.so (raises OSError if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise OSError("libconv3d.so not built at %s: run python -m convolution_implicit_gemm_amd.build"
+                      % path)
+    lib = ctypes.CDLL(path)
+    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    lib.conv3d_plan.argtypes = [ctypes.POINTER(conv3d_desc), ctypes.POINTER(vp), ctypes.POINTER(sz)]
+    lib.conv3d_plan.restype = ctypes.c_int
+    lib.conv3d_plan_query.argtypes = [vp, ctypes.POINTER(conv3d_plan_info)]
+    lib.conv3d_plan_query.restype = ctypes.c_int
+    lib.conv3d_plan_destroy.argtypes = [vp]
+    lib.conv3d_plan_destroy.restype = None
+    lib.conv3d_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.conv3d_forward.restype = ctypes.c_int
+    lib.groupnorm_silu_workspace.argtypes = [i32, i64, i32, i32]
+    lib.groupnorm_silu_workspace.restype = sz
+    lib.groupnorm_silu.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_float, i32, vp, sz, vp]
+    lib.groupnorm_silu.restype = ctypes.c_int
+    lib.conv3d_status_str.argtypes = [ctypes.c_int]
+    lib.conv3d_status_str.restype = ctypes.c_char_p
+    lib.conv3d_last_error.argtypes = []
+    lib.conv3d_last_error.restype = ctypes.c_char_p
+    lib.conv3d_version.argtypes = []
+    lib.conv3d_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != CONV3D_OK:
+        raise Conv3dError(status, load_library().conv3d_last_error().decode())
+
+
+def _addr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class Plan:
+    """Owns a conv3d_plan_t; destroyed with the object."""
+
+    def __init__(self, handle, workspace_bytes, desc):
+        self.handle = handle
+        self.workspace_bytes = workspace_bytes
+        self.desc = desc
+
+    def info(self) -> conv3d_plan_info:
+        return conv3d_plan_query(self)
+
+    def __del__(self):
+        if self.handle and _lib is not None:
+            _lib.conv3d_plan_destroy(self.handle)
+            self.handle = None
+
+
+def make_desc(n, t, h, w, c_in, c_out, kt=3, kh=3, kw=3, pad_t_front=1, pad_t_back=1, pad_h=1,
+              pad_w=1, t_pad_mode=CONV3D_TPAD_ZERO, flags=0) -> conv3d_desc:
+    return conv3d_desc(n, t, h, w, c_in, c_out, kt, kh, kw, pad_t_front, pad_t_back, pad_h, pad_w,
+                       t_pad_mode, flags)
+
+
+def conv3d_plan(desc: conv3d_desc) -> Plan:
+    lib = load_library()
+    h = ctypes.c_void_p()
+    ws = ctypes.c_size_t()
+    _check(lib.conv3d_plan(ctypes.byref(desc), ctypes.byref(h), ctypes.byref(ws)))
+    return Plan(h.value, ws.value, desc)
+
+
+def conv3d_plan_query(plan: Plan) -> conv3d_plan_info:
+    info = conv3d_plan_info()
+    _check(load_library().conv3d_plan_query(plan.handle, ctypes.byref(info)))
+    return info
+
+
+def conv3d_plan_destroy(plan: Plan) -> None:
+    if plan.handle:
+        load_library().conv3d_plan_destroy(plan.handle)
+        plan.handle = None
+
+
+def conv3d_forward(plan: Plan, x, weight, bias, residual, y, workspace=None, workspace_bytes=None,
+                   stream=None) -> None:
+    """Enqueue y = conv3d(x, weight) (+bias) (+residual) on ``stream``."""
+    if workspace_bytes is None:
+        if workspace is None:
+            workspace_bytes = 0
+        elif isinstance(workspace, int):
+            workspace_bytes = plan.workspace_bytes
+        else:
+            workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().conv3d_forward(plan.handle, _addr(x), _addr(weight), _addr(bias),
+                                         _addr(residual), _addr(y), _addr(workspace),
+                                         workspace_bytes, _stream(stream)))
+
+
+def groupnorm_silu_workspace(n, thw, c, groups) -> int:
+    return load_library().groupnorm_silu_workspace(n, thw, c, groups)
+
+
+def groupnorm_silu(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, workspace,
+                   workspace_bytes=None, stream=None) -> None:
+    """Enqueue y = [SiLU](GroupNorm(x)) on ``stream``; workspace zero-filled before first use."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().groupnorm_silu(_addr(x), _addr(gamma), _addr(beta), _addr(y), n, thw, c,
+                                         groups, float(eps), 1 if apply_silu else 0,
+                                         _addr(workspace), workspace_bytes, _stream(stream)))
+
+
+def conv3d_status_str(status: int) -> str:
+    return load_library().conv3d_status_str(status).decode()
+
+
+def conv3d_last_error() -> str:
+    return load_library().conv3d_last_error().decode()
+
+
+def conv3d_version() -> int:
+    return load_library().conv3d_version()

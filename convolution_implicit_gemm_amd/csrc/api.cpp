@@ -1,0 +1,341 @@
+// Host side of the C ABI declared in include/conv3d.h: validation, planning
+// (path and tile choice), and launches on the caller's stream.  Nothing here
+// synchronises the device or allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+
+#include "c3d_internal.h"
+#include "conv3d.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+conv3d_status fail(conv3d_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+conv3d_status ok() {
+    g_last_error[0] = '\0';
+    return CONV3D_OK;
+}
+
+constexpr int64_t kMaxVoxels = (int64_t)1 << 30;
+constexpr int kMaxSpatial = 8192;
+constexpr int kMaxKernel = 7;
+constexpr int kMaxChannels = 65536;
+constexpr int kCUs = 256;
+constexpr size_t kLdsPerCU = 160 * 1024;
+
+bool env_is(const char *name, const char *value) {
+    const char *v = getenv(name);
+    return v && strcmp(v, value) == 0;
+}
+
+// gfx950 check, cached per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+conv3d_status check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) return fail(CONV3D_ERR_NO_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+    if (dev >= kMaxDevices) return CONV3D_OK;
+    int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    if (st != 1) return fail(CONV3D_ERR_NO_DEVICE, "device %d is not gfx950 (MI355X)", dev);
+    return CONV3D_OK;
+}
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Relative cost of a tile shape per unit of MFMA work: bigger tiles reuse
+// each LDS byte more often.  Used only to rank candidates.
+double tile_efficiency(const c3d::TileCfg &t) {
+    const double area = (double)t.bm * t.bn;
+    if (area >= 65536) return 1.0;
+    if (area >= 32768) return 0.9;
+    if (area >= 16384) return 0.8;
+    if (area >= 8192) return 0.6;
+    return 0.45;
+}
+
+}  // namespace
+
+struct conv3d_plan_s {
+    conv3d_desc d;
+    int path;
+    c3d::ConvParams prm;  // pointers filled per call
+    const c3d::TileCfg *tile;
+    bool tail;
+    int fold_lo, fold_hi;
+    int64_t fold_khwc;
+    size_t ws_bytes;
+    int64_t x_elems, w_elems, y_elems;
+    double flops;
+};
+
+extern "C" {
+
+const char *conv3d_status_str(conv3d_status s) {
+    switch (s) {
+        case CONV3D_OK: return "ok";
+        case CONV3D_ERR_INVALID_ARG: return "invalid argument";
+        case CONV3D_ERR_UNSUPPORTED: return "unsupported";
+        case CONV3D_ERR_WORKSPACE: return "workspace too small";
+        case CONV3D_ERR_NO_DEVICE: return "no usable gfx950 device";
+        case CONV3D_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *conv3d_last_error(void) { return g_last_error; }
+
+int32_t conv3d_version(void) { return 100; }
+
+conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *workspace_bytes) {
+    if (!d || !out || !workspace_bytes) return fail(CONV3D_ERR_INVALID_ARG, "null argument");
+    *out = nullptr;
+    *workspace_bytes = 0;
+    if (d->n < 1 || d->t < 1 || d->h < 1 || d->w < 1 || d->c_in < 1 || d->c_out < 1)
+        return fail(CONV3D_ERR_INVALID_ARG, "extents must be positive");
+    if (d->kt < 1 || d->kh < 1 || d->kw < 1) return fail(CONV3D_ERR_INVALID_ARG, "kernel extents must be positive");
+    if (d->pad_t_front < 0 || d->pad_t_back < 0 || d->pad_h < 0 || d->pad_w < 0)
+        return fail(CONV3D_ERR_INVALID_ARG, "padding must be non-negative");
+    if (d->pad_t_front >= d->kt || d->pad_t_back >= d->kt || d->pad_h >= d->kh || d->pad_w >= d->kw)
+        return fail(CONV3D_ERR_INVALID_ARG, "padding must be smaller than the kernel extent");
+    if (d->t_pad_mode != CONV3D_TPAD_ZERO && d->t_pad_mode != CONV3D_TPAD_REPLICATE)
+        return fail(CONV3D_ERR_INVALID_ARG, "unknown t_pad_mode %d", d->t_pad_mode);
+    const uint32_t known = CONV3D_F_BIAS | CONV3D_F_RESIDUAL | CONV3D_F_NO_T1_FASTPATH;
+    if (d->flags & ~known) return fail(CONV3D_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags & ~known);
+    const int To = d->t + d->pad_t_front + d->pad_t_back - d->kt + 1;
+    const int Ho = d->h + 2 * d->pad_h - d->kh + 1;
+    const int Wo = d->w + 2 * d->pad_w - d->kw + 1;
+    if (To < 1 || Ho < 1 || Wo < 1) return fail(CONV3D_ERR_INVALID_ARG, "empty output");
+    if (d->c_in % 8 || d->c_out % 8)
+        return fail(CONV3D_ERR_UNSUPPORTED, "c_in and c_out must be multiples of 8 (got %d, %d)", d->c_in, d->c_out);
+    if (d->c_in > kMaxChannels || d->c_out > kMaxChannels)
+        return fail(CONV3D_ERR_UNSUPPORTED, "more than %d channels", kMaxChannels);
+    if (d->kt > kMaxKernel || d->kh > kMaxKernel || d->kw > kMaxKernel)
+        return fail(CONV3D_ERR_UNSUPPORTED, "kernel extents above %d", kMaxKernel);
+    if (d->h > kMaxSpatial || d->w > kMaxSpatial || Ho > kMaxSpatial || Wo > kMaxSpatial)
+        return fail(CONV3D_ERR_UNSUPPORTED, "spatial extents above %d", kMaxSpatial);
+    const int64_t in_vox = (int64_t)d->n * d->t * d->h * d->w;
+    const int64_t out_vox = (int64_t)d->n * To * Ho * Wo;
+    if (in_vox >= kMaxVoxels || out_vox >= kMaxVoxels)
+        return fail(CONV3D_ERR_UNSUPPORTED, "more than 2^30 voxels");
+
+    conv3d_plan_s *p = new (std::nothrow) conv3d_plan_s();
+    if (!p) return fail(CONV3D_ERR_INVALID_ARG, "out of host memory");
+    p->d = *d;
+    p->x_elems = in_vox * d->c_in;
+    p->w_elems = (int64_t)d->c_out * d->kt * d->kh * d->kw * d->c_in;
+    p->y_elems = out_vox * d->c_out;
+
+    const bool force_general = (d->flags & CONV3D_F_NO_T1_FASTPATH) || env_is("CONV3D_FORCE_PATH", "general");
+    int path = CONV3D_PATH_GENERAL;
+    if (!force_general && d->t == 1 && To == 1 && d->kt > 1) {
+        path = CONV3D_PATH_T1_FOLD;
+        if (d->t_pad_mode == CONV3D_TPAD_REPLICATE) {
+            p->fold_lo = 0;  // every tap reads the clamped frame
+            p->fold_hi = d->kt - 1;
+        } else {
+            p->fold_lo = p->fold_hi = d->pad_t_front;  // the only tap inside [0, 1)
+        }
+        p->fold_khwc = (int64_t)d->kh * d->kw * d->c_in;
+        p->ws_bytes = ((size_t)d->c_out * p->fold_khwc * 2 + 255) & ~(size_t)255;
+    } else if (d->kt == 1 && d->kh == 1 && d->kw == 1) {
+        path = CONV3D_PATH_POINTWISE;
+    }
+    p->path = path;
+
+    c3d::ConvParams &q = p->prm;
+    q.T = path == CONV3D_PATH_T1_FOLD ? 1 : d->t;
+    q.H = d->h;
+    q.W = d->w;
+    q.Cin = d->c_in;
+    q.Cout = d->c_out;
+    q.To = To;
+    q.Ho = Ho;
+    q.Wo = Wo;
+    q.kt = path == CONV3D_PATH_T1_FOLD ? 1 : d->kt;
+    q.kh = d->kh;
+    q.kw = d->kw;
+    q.ptf = path == CONV3D_PATH_T1_FOLD ? 0 : d->pad_t_front;
+    q.ph = d->pad_h;
+    q.pw = d->pad_w;
+    q.replicate = d->t_pad_mode == CONV3D_TPAD_REPLICATE ? 1 : 0;
+    q.K = q.kt * q.kh * q.kw * q.Cin;
+    q.M = out_vox;
+
+    // tile choice: forced by CONV3D_TILE, else the cheapest by a wave model
+    int ntile = 0;
+    const c3d::TileCfg *tiles = c3d::tile_table(&ntile);
+    const char *forced = getenv("CONV3D_TILE");
+    const c3d::TileCfg *best = nullptr;
+    double best_cost = 0.0;
+    for (int i = 0; i < ntile; ++i) {
+        const c3d::TileCfg &t = tiles[i];
+        if (forced && *forced) {
+            if (strcmp(forced, t.name) == 0) best = &t;
+            continue;
+        }
+        const int64_t mt = (q.M + t.bm - 1) / t.bm, nt = (q.Cout + t.bn - 1) / t.bn;
+        const int64_t ntiles = mt * nt;
+        int occ = (int)(kLdsPerCU / t.lds_bytes);
+        if (occ > 2048 / t.threads) occ = 2048 / t.threads;
+        if (occ < 1) occ = 1;
+        const int64_t slots = (int64_t)kCUs * occ;
+        const int64_t waves = (ntiles + slots - 1) / slots;
+        const int cpt = (q.Cin + t.bk - 1) / t.bk;
+        const double kwork = (double)q.kt * q.kh * q.kw * cpt * t.bk;
+        const double cost = (double)waves * occ * t.bm * t.bn * kwork / tile_efficiency(t);
+        if (!best || cost < best_cost) {
+            best = &t;
+            best_cost = cost;
+        }
+    }
+    if (!best) {
+        delete p;
+        return fail(CONV3D_ERR_INVALID_ARG, "CONV3D_TILE=%s names no tile configuration", forced);
+    }
+    p->tile = best;
+    p->tail = (q.Cin % best->bk) != 0;
+    q.cpt = (q.Cin + best->bk - 1) / best->bk;
+    q.niter = q.kt * q.kh * q.kw * q.cpt;
+    q.m_tiles = (int)((q.M + best->bm - 1) / best->bm);
+    q.n_tiles = (q.Cout + best->bn - 1) / best->bn;
+    q.tiles = (int64_t)q.m_tiles * q.n_tiles;
+    p->flops = 2.0 * (double)q.M * q.Cout * q.K;
+
+    *out = p;
+    *workspace_bytes = p->ws_bytes;
+    return ok();
+}
+
+conv3d_status conv3d_plan_query(conv3d_plan_t p, conv3d_plan_info *info) {
+    if (!p || !info) return fail(CONV3D_ERR_INVALID_ARG, "null argument");
+    memset(info, 0, sizeof(*info));
+    info->path = p->path;
+    info->t_out = p->prm.To;
+    info->h_out = p->prm.Ho;
+    info->w_out = p->prm.Wo;
+    info->gemm_m = p->prm.M;
+    info->gemm_n = p->prm.Cout;
+    info->gemm_k = p->prm.K;
+    info->flops = p->flops;
+    info->tile_m = p->tile->bm;
+    info->tile_n = p->tile->bn;
+    info->tile_k = p->tile->bk;
+    info->stages = p->tile->stages;
+    info->threads = p->tile->threads;
+    info->grid = p->prm.tiles;
+    info->workspace_bytes = p->ws_bytes;
+    snprintf(info->kernel_name, sizeof(info->kernel_name), "conv3d_igemm_%s%s", p->tile->name,
+             p->tail ? "_tail" : "");
+    return ok();
+}
+
+void conv3d_plan_destroy(conv3d_plan_t p) { delete p; }
+
+conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight, const void *bias,
+                             const void *residual, void *y, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    if (!p) return fail(CONV3D_ERR_INVALID_ARG, "null plan");
+    const bool has_bias = p->d.flags & CONV3D_F_BIAS, has_res = p->d.flags & CONV3D_F_RESIDUAL;
+    if (!x || !weight || !y) return fail(CONV3D_ERR_INVALID_ARG, "x, weight and y are required");
+    if (has_bias && !bias) return fail(CONV3D_ERR_INVALID_ARG, "plan has CONV3D_F_BIAS but bias is null");
+    if (has_res && !residual) return fail(CONV3D_ERR_INVALID_ARG, "plan has CONV3D_F_RESIDUAL but residual is null");
+    if (misaligned(x) || misaligned(weight) || misaligned(y) || (has_bias && misaligned(bias)) ||
+        (has_res && misaligned(residual)) || (workspace && misaligned(workspace)))
+        return fail(CONV3D_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    const size_t yb = (size_t)p->y_elems * 2;
+    if (overlap(y, yb, x, (size_t)p->x_elems * 2) || overlap(y, yb, weight, (size_t)p->w_elems * 2) ||
+        (has_bias && overlap(y, yb, bias, (size_t)p->d.c_out * 2)) || (has_res && overlap(y, yb, residual, yb)))
+        return fail(CONV3D_ERR_INVALID_ARG, "y overlaps an input");
+    if (p->ws_bytes) {
+        if (!workspace || workspace_bytes < p->ws_bytes)
+            return fail(CONV3D_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p->ws_bytes,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (overlap(workspace, p->ws_bytes, y, yb) || overlap(workspace, p->ws_bytes, x, (size_t)p->x_elems * 2) ||
+            overlap(workspace, p->ws_bytes, weight, (size_t)p->w_elems * 2))
+            return fail(CONV3D_ERR_INVALID_ARG, "workspace overlaps a tensor");
+    }
+    conv3d_status st = check_device();
+    if (st != CONV3D_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    c3d::ConvParams q = p->prm;
+    q.x = static_cast<const _Float16 *>(x);
+    q.w = static_cast<const _Float16 *>(weight);
+    q.bias = has_bias ? static_cast<const _Float16 *>(bias) : nullptr;
+    q.res = has_res ? static_cast<const _Float16 *>(residual) : nullptr;
+    q.y = static_cast<_Float16 *>(y);
+    if (p->path == CONV3D_PATH_T1_FOLD) {
+        _Float16 *w2 = static_cast<_Float16 *>(workspace);
+        hipError_t e = c3d::launch_fold_taps(q.w, w2, p->d.c_out, p->d.kt, p->fold_khwc, p->fold_lo, p->fold_hi, s);
+        if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "fold launch: %s", hipGetErrorString(e));
+        q.w = w2;
+    }
+    hipError_t e = (p->tail ? p->tile->launch_tail : p->tile->launch_full)(q, s);
+    if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "conv launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t groupnorm_silu_workspace(int32_t n, int64_t thw, int32_t c, int32_t groups) {
+    if (n < 1 || thw < 1 || c < 8 || groups < 1 || c % groups || (c / groups) % 8 || c > 8192) return 0;
+    return c3d::gn_workspace_bytes(n, thw, c, groups);
+}
+
+conv3d_status groupnorm_silu(const void *x, const void *gamma, const void *beta, void *y, int32_t n, int64_t thw,
+                             int32_t c, int32_t groups, float eps, int32_t apply_silu, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    if (!x || !gamma || !beta || !y) return fail(CONV3D_ERR_INVALID_ARG, "x, gamma, beta and y are required");
+    if (n < 1 || thw < 1 || c < 1 || groups < 1) return fail(CONV3D_ERR_INVALID_ARG, "sizes must be positive");
+    if (c % groups) return fail(CONV3D_ERR_INVALID_ARG, "c (%d) is not a multiple of groups (%d)", c, groups);
+    if (!(eps >= 0.0f)) return fail(CONV3D_ERR_INVALID_ARG, "eps must be non-negative");
+    if ((c / groups) % 8 || c > 8192)
+        return fail(CONV3D_ERR_UNSUPPORTED, "channels per group must be a multiple of 8 and c <= 8192");
+    if ((int64_t)n * thw >= ((int64_t)1 << 40)) return fail(CONV3D_ERR_UNSUPPORTED, "tensor too large");
+    if (misaligned(x) || misaligned(y) || misaligned(workspace) || (reinterpret_cast<uintptr_t>(gamma) & 1) ||
+        (reinterpret_cast<uintptr_t>(beta) & 1))
+        return fail(CONV3D_ERR_INVALID_ARG, "x, y and workspace must be 16-byte aligned");
+    const size_t bytes = (size_t)n * thw * c * 2;
+    if (x != y && overlap(x, bytes, y, bytes)) return fail(CONV3D_ERR_INVALID_ARG, "x and y partially overlap");
+    const size_t need = c3d::gn_workspace_bytes(n, thw, c, groups);
+    if (!workspace || workspace_bytes < need)
+        return fail(CONV3D_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    conv3d_status st = check_device();
+    if (st != CONV3D_OK) return st;
+    hipError_t e = c3d::launch_groupnorm_silu(static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(gamma),
+                                              static_cast<const _Float16 *>(beta), static_cast<_Float16 *>(y), n, thw,
+                                              c, groups, eps, apply_silu, workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "groupnorm launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal interfaces between the host-side C ABI (api.cpp) and the gfx950
+// kernels.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace c3d {
+
+// Everything the implicit-GEMM kernel needs, passed by value as the kernel
+// argument.  Extents are of the conv as executed (after a temporal fold the
+// kernel sees kt = 1 and T = 1).
+struct ConvParams {
+    const _Float16 *x;     // [N][T][H][W][Cin]
+    const _Float16 *w;     // [Cout][kt][kh][kw][Cin]
+    const _Float16 *bias;  // [Cout] or null
+    const _Float16 *res;   // [M][Cout] or null
+    _Float16 *y;           // [M][Cout]
+    int32_t T, H, W, Cin, Cout;
+    int32_t To, Ho, Wo;
+    int32_t kt, kh, kw, ptf, ph, pw, replicate;
+    int32_t K;             // kt*kh*kw*Cin
+    int32_t cpt;           // K-iterations per tap: ceil(Cin / BK)
+    int32_t niter;         // kt*kh*kw*cpt
+    int32_t m_tiles, n_tiles;
+    int64_t M;             // N*To*Ho*Wo
+    int64_t tiles;         // m_tiles*n_tiles
+};
+
+typedef hipError_t (*ConvLaunchFn)(const ConvParams &p, hipStream_t s);
+
+// One compiled tile configuration of the implicit-GEMM kernel.
+struct TileCfg {
+    const char *name;
+    int bm, bn, bk, stages, threads;
+    size_t lds_bytes;
+    ConvLaunchFn launch_full;  // Cin % bk == 0
+    ConvLaunchFn launch_tail;  // any Cin % 8 == 0 (channel tail zero-filled per tap)
+};
+
+const TileCfg *tile_table(int *count);
+
+// Sum of the temporal taps tau in [tau_lo, tau_hi] of w [Cout][kt][khw*Cin]
+// into w2 [Cout][khw*Cin], in fp32, rounded once to fp16.
+hipError_t launch_fold_taps(const _Float16 *w, _Float16 *w2, int32_t cout, int32_t kt,
+                            int64_t khw_cin, int32_t tau_lo, int32_t tau_hi, hipStream_t s);
+
+// GroupNorm(+SiLU): workspace layout and launch.
+size_t gn_workspace_bytes(int32_t n, int64_t thw, int32_t c, int32_t groups);
+hipError_t launch_groupnorm_silu(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta,
+                                 _Float16 *y, int32_t n, int64_t thw, int32_t c, int32_t groups,
+                                 float eps, int32_t silu, void *ws, hipStream_t s);
+
+}  // namespace c3d

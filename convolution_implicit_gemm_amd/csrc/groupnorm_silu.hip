@@ -1,0 +1,284 @@
+// GroupNorm (+SiLU) over channels-last fp16 activations, for gfx950.
+//
+// The fused GroupNorm+SiLU of a 3D ResNet decoder block (A1111 Metal fork
+// write-up, news.bugfactory.tech item 4286, paragraph on MPS tweaks).  Both
+// passes are HBM-bound streams, so the design is about coalescing, not math:
+//
+//  stats:  grid (SB, N).  Every thread reads 16-byte vectors (8 channels of
+//          one group) of consecutive voxels, so a block reads one contiguous
+//          range.  The thread count is a multiple of C/8, so each thread keeps
+//          one group and accumulates in registers with the shifted-data
+//          method (sums of x-K and (x-K)^2 about its first value K, fp32),
+//          then the block merges threads of a group (Chan's pairwise
+//          update) and writes (count, mean, M2) partials.  The last block to
+//          finish (device-scope counter) merges the SB partials of each
+//          (sample, group) with one wavefront per pair, and writes
+//          per-channel scale a = gamma*rstd and shift b = beta - mean*a.
+//  apply:  grid (AB, N).  Each thread owns one channel vector, keeps its 8
+//          scales/shifts in registers, and streams y = x*a + b, then
+//          y*sigmoid(y), rounded once to fp16.
+#include "c3d_internal.h"
+
+namespace c3d {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+namespace {
+
+constexpr int kMaxThreads = 1024;
+
+struct GnGeom {
+    int vpv;        // 16-byte vectors per voxel (C/8)
+    int threads;    // stats/apply block size: a multiple of vpv
+    int sb;         // stats blocks per sample
+    int ab;         // apply blocks per sample
+};
+
+GnGeom gn_geom(int32_t n, int64_t thw, int32_t c) {
+    GnGeom g;
+    g.vpv = c / 8;
+    // a multiple of vpv (one channel vector per thread), of 64 where that fits
+    // in a block, and at least 256 threads where vpv allows
+    int t = g.vpv;
+    while (t < 256 && t + g.vpv <= kMaxThreads) t += g.vpv;
+    int t64 = t;
+    while (t64 % 64 && t64 + g.vpv <= kMaxThreads) t64 += g.vpv;
+    g.threads = (t64 % 64 == 0) ? t64 : t;
+    const int vox_per_pass = g.threads / g.vpv;
+    // about 2048 stats blocks over the whole tensor, each at least 4 passes deep
+    int64_t want = (2048 + n - 1) / n;
+    int64_t maxb = (thw + 4 * vox_per_pass - 1) / (4 * vox_per_pass);
+    g.sb = (int)(want < maxb ? want : maxb);
+    if (g.sb < 1) g.sb = 1;
+    int64_t wanta = (4096 + n - 1) / n;
+    int64_t maxa = (thw + 2 * vox_per_pass - 1) / (2 * vox_per_pass);
+    g.ab = (int)(wanta < maxa ? wanta : maxa);
+    if (g.ab < 1) g.ab = 1;
+    return g;
+}
+
+// Workspace layout (bytes): [0,256) counter; then scale/shift [N][C] float x2;
+// then partials [N][SB][G] float4 (count, mean, M2, unused).
+size_t off_scale() { return 256; }
+size_t off_part(int32_t n, int32_t c) {
+    size_t b = 256 + (size_t)n * c * 2 * sizeof(float);
+    return (b + 255) & ~(size_t)255;
+}
+
+struct Welford {
+    float n, mean, m2;
+};
+
+__device__ __forceinline__ Welford chan_merge(Welford a, Welford b) {
+    const float n = a.n + b.n;
+    if (n == 0.0f) return a;
+    const float d = b.mean - a.mean;
+    const float fb = b.n / n;
+    Welford r;
+    r.n = n;
+    r.mean = a.mean + d * fb;
+    r.m2 = a.m2 + b.m2 + d * d * a.n * fb;
+    return r;
+}
+
+__global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(
+    const _Float16 *__restrict__ x, int64_t thw, int32_t c, int32_t groups, int32_t sb, float eps,
+    const _Float16 *__restrict__ gamma, const _Float16 *__restrict__ beta, unsigned *counter,
+    float *__restrict__ scale, float *__restrict__ shift, float4 *__restrict__ part) {
+    __shared__ float4 red[kMaxThreads];
+    __shared__ bool am_last;
+    const int n = blockIdx.y;
+    const int b = blockIdx.x;
+    const int vpv = c / 8;
+    const int vpg = (c / groups) / 8;
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int vi = tid % vpv;
+    const int vox_step = nthr / vpv;
+    const int64_t v_begin = thw * b / sb, v_end = thw * (b + 1) / sb;
+    const half8_t *xs = reinterpret_cast<const half8_t *>(x + (size_t)n * thw * c);
+
+    // shifted-data accumulation about the first value this thread sees
+    float K = 0.0f, s1 = 0.0f, s2 = 0.0f, cnt = 0.0f;
+    bool have_k = false;
+    int64_t v = v_begin + tid / vpv;
+    // four loads in flight per iteration
+    for (; v + 3 * vox_step < v_end; v += 4 * vox_step) {
+        half8_t h[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) h[u] = __builtin_nontemporal_load(xs + (v + u * vox_step) * vpv + vi);
+        if (!have_k) {
+            K = (float)h[0][0];
+            have_k = true;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float d = (float)h[u][q] - K;
+                s1 += d;
+                s2 = fmaf(d, d, s2);
+            }
+        cnt += 32.0f;
+    }
+    for (; v < v_end; v += vox_step) {
+        const half8_t h = __builtin_nontemporal_load(xs + v * vpv + vi);
+        if (!have_k) {
+            K = (float)h[0];
+            have_k = true;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float d = (float)h[q] - K;
+            s1 += d;
+            s2 = fmaf(d, d, s2);
+        }
+        cnt += 8.0f;
+    }
+    Welford w;
+    w.n = cnt;
+    w.mean = cnt > 0.0f ? K + s1 / cnt : 0.0f;
+    w.m2 = cnt > 0.0f ? fmaxf(s2 - s1 * (s1 / cnt), 0.0f) : 0.0f;
+    red[tid] = make_float4(w.n, w.mean, w.m2, 0.0f);
+    __syncthreads();
+
+    // merge the threads of each group: threads t with (t % vpv) / vpg == g
+    for (int g = tid; g < groups; g += nthr) {
+        Welford acc = {0.0f, 0.0f, 0.0f};
+        for (int t = 0; t < nthr; ++t) {
+            if ((t % vpv) / vpg != g) continue;
+            const float4 e = red[t];
+            acc = chan_merge(acc, Welford{e.x, e.y, e.z});
+        }
+        part[((size_t)n * sb + b) * groups + g] = make_float4(acc.n, acc.mean, acc.m2, 0.0f);
+    }
+
+    // last block merges everything
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned total = gridDim.x * gridDim.y;
+        am_last = atomicAdd(counter, 1u) == total - 1;
+    }
+    __syncthreads();
+    if (!am_last) return;
+    __threadfence();
+
+    // only full wavefronts take part: the merge below shuffles across all 64 lanes
+    const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
+    const int pairs = gridDim.y * groups;
+    for (int pidx = wave; wave < nwaves && pidx < pairs; pidx += nwaves) {
+        const int pn = pidx / groups, pg = pidx % groups;
+        Welford acc = {0.0f, 0.0f, 0.0f};
+        // plain loads: the device-scope fence above invalidated this CU's L1
+        for (int bb = lane; bb < sb; bb += 64) {
+            const float4 e = part[((size_t)pn * sb + bb) * groups + pg];
+            acc = chan_merge(acc, Welford{e.x, e.y, e.z});
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            Welford o;
+            o.n = __shfl_xor(acc.n, off);
+            o.mean = __shfl_xor(acc.mean, off);
+            o.m2 = __shfl_xor(acc.m2, off);
+            acc = chan_merge(acc, o);
+        }
+        const float var = acc.m2 / acc.n;
+        const float rstd = 1.0f / sqrtf(var + eps);
+        const int cg = c / groups;
+        for (int cc = lane; cc < cg; cc += 64) {
+            const int ch = pg * cg + cc;
+            const float a = rstd * (float)gamma[ch];
+            scale[(size_t)pn * c + ch] = a;
+            shift[(size_t)pn * c + ch] = (float)beta[ch] - acc.mean * a;
+        }
+    }
+    if (tid == 0) *counter = 0u;  // ready for the next call on this workspace
+}
+
+__device__ __forceinline__ float silu_f32(float y) {
+    // y * sigmoid(y) = y / (1 + 2^(-y*log2(e)))
+    const float e = __builtin_amdgcn_exp2f(-y * 1.4426950408889634f);
+    return y * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+template <bool SILU>
+__global__ __launch_bounds__(kMaxThreads) void gn_apply_kernel(const _Float16 *__restrict__ x,
+                                                              _Float16 *__restrict__ y, int64_t thw,
+                                                              int32_t c, const float *__restrict__ scale,
+                                                              const float *__restrict__ shift) {
+    const int n = blockIdx.y;
+    const int vpv = c / 8;
+    const int tid = threadIdx.x;
+    const int vi = tid % vpv;
+    const int vox_step = (blockDim.x / vpv) * gridDim.x;
+    float a[8], bsh[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        a[q] = scale[(size_t)n * c + vi * 8 + q];
+        bsh[q] = shift[(size_t)n * c + vi * 8 + q];
+    }
+    const half8_t *xs = reinterpret_cast<const half8_t *>(x + (size_t)n * thw * c);
+    half8_t *ys = reinterpret_cast<half8_t *>(y + (size_t)n * thw * c);
+    int64_t v = (int64_t)blockIdx.x * (blockDim.x / vpv) + tid / vpv;
+    for (; v + vox_step < thw; v += 2 * vox_step) {
+        const half8_t h0 = __builtin_nontemporal_load(xs + v * vpv + vi);
+        const half8_t h1 = __builtin_nontemporal_load(xs + (v + vox_step) * vpv + vi);
+        half8_t o0, o1;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            float t0 = fmaf((float)h0[q], a[q], bsh[q]);
+            float t1 = fmaf((float)h1[q], a[q], bsh[q]);
+            if (SILU) {
+                t0 = silu_f32(t0);
+                t1 = silu_f32(t1);
+            }
+            o0[q] = (_Float16)t0;
+            o1[q] = (_Float16)t1;
+        }
+        __builtin_nontemporal_store(o0, ys + v * vpv + vi);
+        __builtin_nontemporal_store(o1, ys + (v + vox_step) * vpv + vi);
+    }
+    for (; v < thw; v += vox_step) {
+        const half8_t h0 = __builtin_nontemporal_load(xs + v * vpv + vi);
+        half8_t o0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            float t0 = fmaf((float)h0[q], a[q], bsh[q]);
+            if (SILU) t0 = silu_f32(t0);
+            o0[q] = (_Float16)t0;
+        }
+        __builtin_nontemporal_store(o0, ys + v * vpv + vi);
+    }
+}
+
+}  // namespace
+
+size_t gn_workspace_bytes(int32_t n, int64_t thw, int32_t c, int32_t groups) {
+    const GnGeom g = gn_geom(n, thw, c);
+    return off_part(n, c) + (size_t)n * g.sb * groups * sizeof(float4);
+}
+
+hipError_t launch_groupnorm_silu(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta, _Float16 *y,
+                                 int32_t n, int64_t thw, int32_t c, int32_t groups, float eps, int32_t silu,
+                                 void *ws, hipStream_t s) {
+    const GnGeom g = gn_geom(n, thw, c);
+    char *base = static_cast<char *>(ws);
+    unsigned *counter = reinterpret_cast<unsigned *>(base);
+    float *scale = reinterpret_cast<float *>(base + off_scale());
+    float *shift = scale + (size_t)n * c;
+    float4 *part = reinterpret_cast<float4 *>(base + off_part(n, c));
+    hipLaunchKernelGGL(gn_stats_kernel, dim3(g.sb, n), dim3(g.threads), 0, s, x, thw, c, groups, g.sb, eps,
+                       gamma, beta, counter, scale, shift, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (silu)
+        hipLaunchKernelGGL(gn_apply_kernel<true>, dim3(g.ab, n), dim3(g.threads), 0, s, x, y, thw, c, scale,
+                           shift);
+    else
+        hipLaunchKernelGGL(gn_apply_kernel<false>, dim3(g.ab, n), dim3(g.threads), 0, s, x, y, thw, c, scale,
+                           shift);
+    return hipGetLastError();
+}
+
+}  // namespace c3d

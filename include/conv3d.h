@@ -1,0 +1,174 @@
+/*
+ * conv3d.h -- C ABI of the MI355X (gfx950) fp16 3D-convolution library.
+ *
+ * The operation is the stride-1 3D cross-correlation of an fp16 NDHWC video
+ * tensor, computed as an implicit GEMM: rows are the M = N*To*Ho*Wo output
+ * voxels, columns the Cout output channels, and the reduction runs over
+ * K = kt*kh*kw*Cin (tap-major, input channel fastest), gathered on the fly so
+ * that no im2col buffer is ever built.  This is the technique of the Draw
+ * Things engineering feed, post on the Codex-written Metal conv3d shaders for
+ * the LTX-2.3 video VAE (implicit-GEMM paragraph).  A causal first frame (T=1
+ * with the first frame replicated in front) collapses to a 2D convolution
+ * with the temporal taps summed, after the "Video VAE" section of the Qwen
+ * Image post on the same feed.  The fused GroupNorm+SiLU of a 3D ResNet
+ * decoder block follows the A1111 Metal fork write-up (news.bugfactory.tech
+ * item 4286, paragraph on MPS tweaks and the fused kernel).
+ *
+ * Conventions shared by every entry point:
+ *  - No entry point aborts, throws or synchronises the device.  Work is
+ *    enqueued on the caller's stream (a hipStream_t passed as void*; NULL is
+ *    the default stream), after the A1111 Metal fork's lesson that a native
+ *    op must go into the framework's current stream without its own commit.
+ *  - The caller owns every device buffer.  The library never allocates
+ *    device memory.  Device pointers must be 16-byte aligned.
+ *  - All tensors are fp16 (IEEE binary16) unless stated; accumulation is fp32.
+ *  - On failure a status other than CONV3D_OK is returned, nothing is
+ *    launched, and conv3d_last_error() holds a message for this thread.
+ */
+#ifndef CONV3D_H
+#define CONV3D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CONV3D_OK = 0,
+    CONV3D_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad extent, aliasing */
+    CONV3D_ERR_UNSUPPORTED = 2, /* a valid request this library does not run: fall back */
+    CONV3D_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    CONV3D_ERR_NO_DEVICE = 4,   /* no usable gfx950 device */
+    CONV3D_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} conv3d_status;
+
+/* Temporal padding.  Spatial padding is always zero. */
+typedef enum {
+    CONV3D_TPAD_ZERO = 0,      /* frames outside [0,T) read as zeros */
+    CONV3D_TPAD_REPLICATE = 1  /* frame index clamped to [0,T-1]: causal video-VAE padding */
+} conv3d_tpad;
+
+/* Descriptor flags. */
+enum {
+    CONV3D_F_BIAS = 1u,            /* add bias[Cout] */
+    CONV3D_F_RESIDUAL = 2u,        /* add residual[N,To,Ho,Wo,Cout] (fp32 add, one rounding) */
+    CONV3D_F_NO_T1_FASTPATH = 4u   /* never fold temporal taps, even when it is exact */
+};
+
+/* Execution paths a plan may choose. */
+typedef enum {
+    CONV3D_PATH_GENERAL = 0,  /* implicit GEMM over all kt*kh*kw taps */
+    CONV3D_PATH_T1_FOLD = 1,  /* T=1 replicate: taps summed into a 2D kernel, then implicit GEMM */
+    CONV3D_PATH_POINTWISE = 2 /* 1x1x1 without padding: a plain streaming GEMM */
+} conv3d_path;
+
+/*
+ * One stride-1, dilation-1, single-group 3D correlation.
+ *   x:        [n][t][h][w][c_in]                      (NDHWC)
+ *   weight:   [c_out][kt][kh][kw][c_in]
+ *   bias:     [c_out]                                  (if CONV3D_F_BIAS)
+ *   residual: [n][t_out][h_out][w_out][c_out]          (if CONV3D_F_RESIDUAL)
+ *   y:        [n][t_out][h_out][w_out][c_out]
+ * with t_out = t + pad_t_front + pad_t_back - kt + 1,
+ *      h_out = h + 2*pad_h - kh + 1,  w_out = w + 2*pad_w - kw + 1, and
+ * y[n,to,ho,wo,co] = bias[co] + residual[...] +
+ *     sum_{tau,r,s,ci} weight[co,tau,r,s,ci] * xhat[n, to+tau-pad_t_front,
+ *                                                  ho+r-pad_h, wo+s-pad_w, ci],
+ * xhat being x inside the tensor, 0 outside in h and w, and in t either 0
+ * (CONV3D_TPAD_ZERO) or x at the clamped frame (CONV3D_TPAD_REPLICATE).
+ */
+typedef struct {
+    int32_t n, t, h, w, c_in, c_out;
+    int32_t kt, kh, kw;
+    int32_t pad_t_front, pad_t_back, pad_h, pad_w;
+    int32_t t_pad_mode; /* conv3d_tpad */
+    uint32_t flags;     /* CONV3D_F_* */
+} conv3d_desc;
+
+/* A plan is a host-only, immutable object: safe to share between threads. */
+typedef struct conv3d_plan_s *conv3d_plan_t;
+
+/* What a plan chose; filled by conv3d_plan_query. */
+typedef struct {
+    int32_t path;                 /* conv3d_path */
+    int32_t t_out, h_out, w_out;
+    int64_t gemm_m, gemm_n, gemm_k; /* the GEMM as executed (K folded on CONV3D_PATH_T1_FOLD) */
+    double flops;                 /* 2*gemm_m*gemm_n*gemm_k */
+    int32_t tile_m, tile_n, tile_k, stages, threads;
+    int64_t grid;                 /* workgroups of the main kernel */
+    size_t workspace_bytes;
+    char kernel_name[64];         /* the main kernel's symbol stem */
+} conv3d_plan_info;
+
+/*
+ * Validate *d and choose a path and tile configuration.  Host only: needs no
+ * device.  On success *out receives a new plan and *workspace_bytes the
+ * device workspace conv3d_forward needs (0 if none).
+ * Errors: INVALID_ARG for null pointers, non-positive extents, negative or
+ * too-large padding (a pad must be smaller than its kernel extent), an empty
+ * output, or an unknown t_pad_mode / flag bit; UNSUPPORTED for c_in or c_out
+ * not a multiple of 8, kernel extents above 7, spatial extents above 8192,
+ * or 2^30 or more input or output voxels.
+ * The environment variable CONV3D_FORCE_PATH=general behaves like
+ * CONV3D_F_NO_T1_FASTPATH; CONV3D_TILE=<name> forces a tile configuration.
+ */
+conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *workspace_bytes);
+
+/* Fill *info for plan p.  INVALID_ARG if either pointer is null. */
+conv3d_status conv3d_plan_query(conv3d_plan_t p, conv3d_plan_info *info);
+
+/* Release a plan (NULL is ignored). */
+void conv3d_plan_destroy(conv3d_plan_t p);
+
+/*
+ * Enqueue y = conv3d(x, weight) (+bias) (+residual) on stream.
+ * x, weight, y: required device pointers.  bias / residual: required when the
+ * plan's flags say so, otherwise ignored.  workspace: device memory of at
+ * least the planned size (may be NULL when that size is 0); its contents are
+ * scratch, overwritten by each call.  Calls on different streams must not
+ * share a workspace.  y must not overlap x, weight, bias or residual.
+ * Errors: INVALID_ARG (null/misaligned pointers, y aliasing an input),
+ * WORKSPACE (workspace_bytes below the planned size), HIP (launch failure).
+ */
+conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight, const void *bias,
+                             const void *residual, void *y, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * GroupNorm + optional SiLU over channels-last fp16 data.
+ *   x, y:   [n][thw][c]   (thw = T*H*W voxels per sample)
+ *   gamma, beta: [c] fp16
+ * For each sample and each group of c/groups contiguous channels: mean and
+ * biased variance in fp32 over thw*c/groups elements, then
+ * yhat = (x-mean)*rsqrt(var+eps)*gamma + beta, and y = yhat*sigmoid(yhat) if
+ * apply_silu else yhat, rounded once to fp16.  y may equal x (in place).
+ * groupnorm_silu_workspace() gives the workspace bytes (fp32 partial
+ * statistics and per-channel scale/shift; it also holds a counter that each
+ * call leaves at zero, so a workspace must be zero-filled once before its
+ * first use and must not be shared by calls that may run concurrently).
+ * Errors: INVALID_ARG (null/misaligned pointers, non-positive sizes,
+ * c % groups != 0, eps < 0), UNSUPPORTED ((c/groups) % 8 != 0, or c > 8192),
+ * WORKSPACE, HIP.
+ */
+size_t groupnorm_silu_workspace(int32_t n, int64_t thw, int32_t c, int32_t groups);
+conv3d_status groupnorm_silu(const void *x, const void *gamma, const void *beta, void *y,
+                             int32_t n, int64_t thw, int32_t c, int32_t groups, float eps,
+                             int32_t apply_silu, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Static text for a status code. */
+const char *conv3d_status_str(conv3d_status s);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char *conv3d_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t conv3d_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV3D_H */

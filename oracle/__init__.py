@@ -62,7 +62,8 @@ def _load():
         i = ctypes.c_int
         lib.oracle_conv3d.argtypes = [d, d, d, d] + [i] * 14 + [d, d]
         lib.oracle_conv3d.restype = i
-        lib.oracle_conv3d_points.argtypes = ([d, d, d, d] + [i] * 14 +
+        vp = ctypes.c_void_p
+        lib.oracle_conv3d_points.argtypes = ([vp, i, d, d, vp, i] + [i] * 14 +
                                              [ctypes.POINTER(ctypes.c_int64),
                                               ctypes.POINTER(ctypes.c_int32),
                                               ctypes.c_int64, d, d])
@@ -70,6 +71,8 @@ def _load():
         lib.oracle_groupnorm_silu.argtypes = [d, i, ctypes.c_int64, i, i, d, d, ctypes.c_double,
                                               i, d, d, d]
         lib.oracle_groupnorm_silu.restype = i
+        lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_f64.restype = ctypes.c_double
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i
         _lib = lib
@@ -125,24 +128,46 @@ def conv3d(x, w, b=None, res=None, pads=(1, 1, 1, 1), tmode=TPAD_ZERO, with_mag=
     return y, mag
 
 
+def _maybe_f16(a):
+    """(pointer, is_f16, keepalive) for an fp16 array passed as raw bits, else fp64."""
+    if a is None:
+        return None, 0, None
+    a = np.asarray(a)
+    if a.dtype == np.float16:
+        a = np.ascontiguousarray(a)
+        return a.ctypes.data_as(ctypes.c_void_p), 1, a
+    a = _f64(a)
+    return a.ctypes.data_as(ctypes.c_void_p), 0, a
+
+
+def f16_to_f64(bits: int) -> float:
+    """The oracle's exact binary16 decoder (exposed for its pin)."""
+    return _load().oracle_f16_to_f64(bits)
+
+
 def conv3d_points(x, w, b, res, pads, tmode, m_idx, co_idx):
     """conv3d at selected outputs: flat voxel index m_idx[i], channel co_idx[i].
 
-    Returns (y[i], S[i]).  x, w, b, res as in conv3d (res: full tensor or None).
+    Returns (y[i], S[i]).  x and res (full residual tensor or None) may be
+    float16 numpy arrays, read in place and widened exactly in C, so that
+    multi-GB activations need no fp64 copy; w and b are widened here.
     """
-    x, w, b, res = _f64(x), _f64(w), _f64(b), _f64(res)
-    n, t, h, wd, cin = x.shape
+    xp, xh, xkeep = _maybe_f16(x)
+    rp, rh, rkeep = _maybe_f16(res)
+    w, b = _f64(w), _f64(b)
+    n, t, h, wd, cin = xkeep.shape
     cout, kt, kh, kw, _ = w.shape
     m_idx = np.ascontiguousarray(m_idx, dtype=np.int64)
     co_idx = np.ascontiguousarray(co_idx, dtype=np.int32)
     y = np.empty(m_idx.shape[0], np.float64)
     mag = np.empty(m_idx.shape[0], np.float64)
     rc = _load().oracle_conv3d_points(
-        _ptr(x), _ptr(w), _ptr(b), _ptr(res), n, t, h, wd, cin, cout, kt, kh, kw,
+        xp, xh, _ptr(w), _ptr(b), rp, rh, n, t, h, wd, cin, cout, kt, kh, kw,
         pads[0], pads[1], pads[2], pads[3], tmode,
         m_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
         co_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
         m_idx.shape[0], _ptr(y), _ptr(mag))
+    del xkeep, rkeep
     if rc != 0:
         raise ValueError("oracle_conv3d_points rejected the input")
     return y, mag

@@ -52,11 +52,27 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/*
+ * IEEE 754 binary16 bit pattern -> double, exactly: sign, 5-bit biased
+ * exponent, 10-bit fraction; subnormals are fraction * 2^-24.
+ */
+double oracle_f16_to_f64(uint16_t h) {
+    int e = (h >> 10) & 31, f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return (h & 0x8000) ? -v : v;
+}
+
 /* Output extent of a stride-1 correlation along one axis. */
 static int out_extent(int in, int pad_lo, int pad_hi, int k) { return in + pad_lo + pad_hi - k + 1; }
 
 /* One output element, straight from the definition.  Returns y and writes S. */
-static double conv_point(const double *x, const double *w, const double *b,
+static double conv_point(const void *xv, int x_f16, const double *w, const double *b,
                          int T, int H, int W, int Cin, int kt, int kh, int kw,
                          int ptf, int ph, int pw, int tmode,
                          int n, int to, int ho, int wo, int co, double *mag) {
@@ -79,12 +95,22 @@ static double conv_point(const double *x, const double *w, const double *b,
             for (int q = 0; q < kw; ++q) {
                 int ws = wo + q - pw;
                 if (ws < 0 || ws >= W) continue;
-                const double *xp = x + ((((size_t)n * T + ts) * H + hs) * W + ws) * (size_t)Cin;
+                size_t xo = ((((size_t)n * T + ts) * H + hs) * W + ws) * (size_t)Cin;
                 const double *wp = w + ((((size_t)co * kt + tau) * kh + r) * kw + q) * (size_t)Cin;
-                for (int ci = 0; ci < Cin; ++ci) {
-                    double p = wp[ci] * xp[ci];
-                    acc += p;
-                    s += fabs(p);
+                if (x_f16) {
+                    const uint16_t *xp = (const uint16_t *)xv + xo;
+                    for (int ci = 0; ci < Cin; ++ci) {
+                        double p = wp[ci] * oracle_f16_to_f64(xp[ci]);
+                        acc += p;
+                        s += fabs(p);
+                    }
+                } else {
+                    const double *xp = (const double *)xv + xo;
+                    for (int ci = 0; ci < Cin; ++ci) {
+                        double p = wp[ci] * xp[ci];
+                        acc += p;
+                        s += fabs(p);
+                    }
                 }
             }
         }
@@ -117,7 +143,7 @@ int oracle_conv3d(const double *x, const double *w, const double *b, const doubl
             size_t base = ((((size_t)n * To + to) * Ho + ho) * Wo + wo) * (size_t)Cout;
             for (int co = 0; co < Cout; ++co) {
                 double s;
-                double v = conv_point(x, w, b, T, H, W, Cin, kt, kh, kw, ptf, ph, pw, tmode,
+                double v = conv_point(x, 0, w, b, T, H, W, Cin, kt, kh, kw, ptf, ph, pw, tmode,
                                       n, to, ho, wo, co, &s);
                 if (res) v += res[base + co];
                 y[base + co] = v;
@@ -130,10 +156,13 @@ int oracle_conv3d(const double *x, const double *w, const double *b, const doubl
 
 /*
  * Selected outputs only, for full-size tensors.  m[i] is the flat output-voxel
- * index ((n*To + to)*Ho + ho)*Wo + wo and co[i] the output channel.  res (if
- * given) is the full residual tensor.  Writes y[i], mag[i].
+ * index ((n*To + to)*Ho + ho)*Wo + wo and co[i] the output channel.  x and
+ * res (the full residual tensor, or NULL) are fp16 bit patterns when
+ * x_f16 / res_f16 is set, doubles otherwise; they are widened exactly.
+ * Writes y[i], mag[i].
  */
-int oracle_conv3d_points(const double *x, const double *w, const double *b, const double *res,
+int oracle_conv3d_points(const void *x, int x_f16, const double *w, const double *b,
+                         const void *res, int res_f16,
                          int N, int T, int H, int W, int Cin, int Cout, int kt, int kh, int kw,
                          int ptf, int ptb, int ph, int pw, int tmode,
                          const int64_t *m, const int32_t *co, int64_t npts, double *y, double *mag) {
@@ -152,9 +181,12 @@ int oracle_conv3d_points(const double *x, const double *w, const double *b, cons
         int to = (int)((mi / ((int64_t)Wo * Ho)) % To);
         int n = (int)(mi / ((int64_t)Wo * Ho * To));
         double s;
-        double v = conv_point(x, w, b, T, H, W, Cin, kt, kh, kw, ptf, ph, pw, tmode,
+        double v = conv_point(x, x_f16, w, b, T, H, W, Cin, kt, kh, kw, ptf, ph, pw, tmode,
                               n, to, ho, wo, co[i], &s);
-        if (res) v += res[(size_t)mi * Cout + co[i]];
+        if (res) {
+            size_t ri = (size_t)mi * Cout + co[i];
+            v += res_f16 ? oracle_f16_to_f64(((const uint16_t *)res)[ri]) : ((const double *)res)[ri];
+        }
         y[i] = v;
         if (mag) mag[i] = s;
     }

@@ -1,0 +1,170 @@
+"""Shared helpers for the GPU parity tests: device I/O, guard bands, bounds.
+
+The acceptance bounds (stated once here, used by every GPU test):
+  conv3d:          |gpu - ref| <= 2e-3 * S + ulp16(ref),
+                   S = |b| + sum |w * xhat| (the oracle's magnitude), and
+                   ulp16(v) = 2^(max(floor(log2|v|), -14) - 10), the fp16
+                   spacing at v.  fp32 accumulation over K <= 13,824 terms
+                   costs at most K * 2^-24 * S ~ 8.2e-4 S; the final RNE
+                   rounding costs half an ulp.
+  groupnorm_silu:  |gpu - ref| <= 1e-3 * |ref| + 2^-14 (the absolute floor,
+                   the smallest fp16 normal, covers SiLU's zero crossing).
+"""
+from __future__ import annotations
+
+import os
+from contextlib import contextmanager
+
+import numpy as np
+import torch
+
+import convolution_implicit_gemm_amd as c3d
+
+GUARD = 64  # fp16 elements of guard band on each side of every output
+GUARD_BITS = 0x7E5A  # a NaN pattern no kernel writes
+
+
+def dev(a):
+    """numpy fp16 -> torch fp16 on cuda:0."""
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def guarded_empty(shape):
+    """(buffer, view): an fp16 device tensor with NaN-patterned guard bands around it."""
+    n = int(np.prod(shape))
+    buf = torch.empty(n + 2 * GUARD, dtype=torch.int16, device="cuda:0")
+    buf.fill_(GUARD_BITS - 65536 if GUARD_BITS > 32767 else GUARD_BITS)
+    view = buf[GUARD:GUARD + n].view(torch.float16).view(shape)
+    return buf, view
+
+
+def check_guards(buf):
+    b = buf.cpu().numpy()
+    want = np.int16(GUARD_BITS - 65536 if GUARD_BITS > 32767 else GUARD_BITS)
+    assert np.all(b[:GUARD] == want), "write before the output tensor"
+    assert np.all(b[-GUARD:] == want), "write past the output tensor"
+
+
+@contextmanager
+def forced_tile(name):
+    old = os.environ.get("CONV3D_TILE")
+    if name:
+        os.environ["CONV3D_TILE"] = name
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("CONV3D_TILE", None)
+        else:
+            os.environ["CONV3D_TILE"] = old
+
+
+def tile_names():
+    """Tile configurations compiled into the library (by forcing each name in turn)."""
+    names = ["m256n256k64s2w4", "m256n256k32s4w4", "m256n256k64s2w8", "m256n128k64s2w4",
+             "m128n128k64s3w4", "m128n64k64s2w4", "m128n32k32s2w4"]
+    return names
+
+
+def conv_desc(shape, flags=0):
+    return c3d.make_desc(shape.n, shape.t, shape.h, shape.w, shape.cin, shape.cout, shape.kt,
+                         shape.kh, shape.kw, shape.pad_t_front, shape.pad_t_back, shape.pad_h,
+                         shape.pad_w, shape.tmode, flags)
+
+
+def out_dims(shape):
+    return (shape.n, shape.t + shape.pad_t_front + shape.pad_t_back - shape.kt + 1,
+            shape.h + 2 * shape.pad_h - shape.kh + 1, shape.w + 2 * shape.pad_w - shape.kw + 1,
+            shape.cout)
+
+
+def run_conv(shape, x, w, b=None, res=None, flags=0, tile=None, keep_device=False):
+    """Run the HIP conv through the C ABI; returns (y fp16 numpy or device tensor, plan info)."""
+    if b is not None:
+        flags |= c3d.CONV3D_F_BIAS
+    if res is not None:
+        flags |= c3d.CONV3D_F_RESIDUAL
+    with forced_tile(tile):
+        plan = c3d.conv3d_plan(conv_desc(shape, flags))
+    info = plan.info()
+    xd = x if isinstance(x, torch.Tensor) else dev(x)
+    wd = w if isinstance(w, torch.Tensor) else dev(w)
+    bd = None if b is None else (b if isinstance(b, torch.Tensor) else dev(b))
+    rd = None if res is None else (res if isinstance(res, torch.Tensor) else dev(res))
+    buf, y = guarded_empty(out_dims(shape))
+    ws = None
+    if plan.workspace_bytes:
+        ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda:0")
+    c3d.conv3d_forward(plan, xd, wd, bd, rd, y, ws)
+    torch.cuda.synchronize()
+    check_guards(buf)
+    if keep_device:
+        return y, info
+    return y.cpu().numpy(), info
+
+
+def ulp16(v):
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.where(a > 0, np.maximum(e, -14), -14)
+    return np.exp2(e - 10)
+
+
+def conv_violations(gpu, ref, mag):
+    """Indices where the conv bound fails, and the worst ratio err / bound."""
+    g = np.asarray(gpu, dtype=np.float64)
+    err = np.abs(g - ref)
+    bound = 2e-3 * mag + ulp16(ref)
+    bad = ~(err <= bound)  # NaN counts as a failure
+    ratio = float(np.max(err / bound)) if err.size else 0.0
+    return np.flatnonzero(bad.reshape(-1)), ratio
+
+
+def assert_conv_close(gpu, ref, mag, what=""):
+    bad, ratio = conv_violations(gpu, ref, mag)
+    if bad.size:
+        g = np.asarray(gpu, dtype=np.float64).reshape(-1)
+        i = bad[0]
+        raise AssertionError("%s: %d of %d outside bound (worst err/bound %.3g); first at %d: "
+                             "gpu %r ref %r S %r" % (what, bad.size, g.size, ratio, i, g[i],
+                                                     np.asarray(ref).reshape(-1)[i],
+                                                     np.asarray(mag).reshape(-1)[i]))
+    return ratio
+
+
+def assert_gn_close(gpu, ref, what=""):
+    g = np.asarray(gpu, dtype=np.float64)
+    err = np.abs(g - ref)
+    bound = 1e-3 * np.abs(ref) + 2.0 ** -14
+    bad = ~(err <= bound)
+    if np.any(bad):
+        i = np.flatnonzero(bad.reshape(-1))[0]
+        raise AssertionError("%s: %d of %d outside bound; first at %d: gpu %r ref %r" % (
+            what, int(bad.sum()), g.size, i, g.reshape(-1)[i], np.asarray(ref).reshape(-1)[i]))
+    return float(np.max(err / bound)) if err.size else 0.0
+
+
+def sample_points(m_total, cout, count, seed, extra_m=()):
+    """Seeded (m, co) sample: `count` random pairs plus every channel at the voxels in extra_m."""
+    rng = np.random.default_rng(seed)
+    m = rng.integers(0, m_total, count)
+    co = rng.integers(0, cout, count)
+    if len(extra_m):
+        em = np.repeat(np.asarray(extra_m, dtype=np.int64), cout)
+        ec = np.tile(np.arange(cout), len(extra_m))
+        m = np.concatenate([m, em])
+        co = np.concatenate([co, ec])
+    return m, co
+
+
+def edge_voxels(odims):
+    """Flat indices of corner/edge voxels of first, second and last frames."""
+    n, t, h, w, _ = odims
+    out = []
+    for nn in {0, n - 1}:
+        for tt in sorted({0, min(1, t - 1), t - 1}):
+            for hh in sorted({0, h // 2, h - 1}):
+                for ww in sorted({0, w // 2, w - 1}):
+                    out.append(((nn * t + tt) * h + hh) * w + ww)
+    return out

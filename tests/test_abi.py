@@ -1,0 +1,170 @@
+"""The C ABI on the host: symbols, planning, validation and error statuses.
+
+No GPU needed: planning is host-only, and every argument check in
+conv3d_forward / groupnorm_silu runs before the device is touched (fake,
+never-dereferenced addresses are enough to reach each status).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import convolution_implicit_gemm_amd as c3d
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "conv3d.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"if", "sizeof"})
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(c3d.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = c3d.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings_and_version():
+    assert c3d.conv3d_status_str(0) == "ok"
+    assert "workspace" in c3d.conv3d_status_str(3)
+    assert c3d.conv3d_version() >= 100
+
+
+def desc(**kw):
+    base = dict(n=1, t=9, h=64, w=64, c_in=512, c_out=512, kt=3, kh=3, kw=3, pad_t_front=2,
+                pad_t_back=0, pad_h=1, pad_w=1, t_pad_mode=c3d.CONV3D_TPAD_REPLICATE,
+                flags=c3d.CONV3D_F_BIAS)
+    base.update(kw)
+    return c3d.make_desc(**base)
+
+
+def plan_status(d):
+    lib = c3d.load_library()
+    h = ctypes.c_void_p()
+    ws = ctypes.c_size_t()
+    st = lib.conv3d_plan(ctypes.byref(d), ctypes.byref(h), ctypes.byref(ws))
+    if st == 0:
+        lib.conv3d_plan_destroy(h)
+    return st
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(n=0), c3d.CONV3D_ERR_INVALID_ARG),
+    (dict(h=-1), c3d.CONV3D_ERR_INVALID_ARG),
+    (dict(kt=0), c3d.CONV3D_ERR_INVALID_ARG),
+    (dict(pad_h=3), c3d.CONV3D_ERR_INVALID_ARG),
+    (dict(pad_t_front=-1), c3d.CONV3D_ERR_INVALID_ARG),
+    (dict(t_pad_mode=7), c3d.CONV3D_ERR_INVALID_ARG),
+    (dict(flags=64), c3d.CONV3D_ERR_INVALID_ARG),
+    (dict(t=1, pad_t_front=0), c3d.CONV3D_ERR_INVALID_ARG),  # empty output
+    (dict(c_in=12), c3d.CONV3D_ERR_UNSUPPORTED),
+    (dict(c_out=4), c3d.CONV3D_ERR_UNSUPPORTED),
+    (dict(kh=9, pad_h=4), c3d.CONV3D_ERR_UNSUPPORTED),
+    (dict(h=9000), c3d.CONV3D_ERR_UNSUPPORTED),
+    (dict(n=64, t=64, h=512, w=512, c_in=8), c3d.CONV3D_ERR_UNSUPPORTED),  # 2^30 voxels
+])
+def test_plan_rejects(bad, status):
+    assert plan_status(desc(**bad)) == status
+    assert c3d.conv3d_last_error() != ""
+
+
+def test_plan_null_arguments():
+    lib = c3d.load_library()
+    assert lib.conv3d_plan(None, None, None) == c3d.CONV3D_ERR_INVALID_ARG
+    assert lib.conv3d_plan_query(None, None) == c3d.CONV3D_ERR_INVALID_ARG
+    lib.conv3d_plan_destroy(None)
+
+
+def test_plan_paths_and_sizes():
+    p = c3d.conv3d_plan(desc())
+    i = p.info()
+    assert i.path == c3d.CONV3D_PATH_GENERAL
+    assert (i.t_out, i.h_out, i.w_out) == (9, 64, 64)
+    assert (i.gemm_m, i.gemm_n, i.gemm_k) == (9 * 64 * 64, 512, 27 * 512)
+    assert i.flops == 2.0 * 36864 * 512 * 13824
+    assert p.workspace_bytes == 0 and i.grid > 0
+
+    p1 = c3d.conv3d_plan(desc(t=1))
+    i1 = p1.info()
+    assert i1.path == c3d.CONV3D_PATH_T1_FOLD and i1.gemm_k == 9 * 512
+    assert p1.workspace_bytes >= 512 * 9 * 512 * 2
+    # the flag and the environment switch both force the general path
+    assert c3d.conv3d_plan(desc(t=1, flags=c3d.CONV3D_F_NO_T1_FASTPATH)).info().path == 0
+    os.environ["CONV3D_FORCE_PATH"] = "general"
+    try:
+        assert c3d.conv3d_plan(desc(t=1)).info().path == 0
+    finally:
+        del os.environ["CONV3D_FORCE_PATH"]
+    # zero-causal first frame folds to its single surviving tap
+    pz = c3d.conv3d_plan(desc(t=1, t_pad_mode=c3d.CONV3D_TPAD_ZERO)).info()
+    assert pz.path == c3d.CONV3D_PATH_T1_FOLD
+    pw = c3d.conv3d_plan(desc(kt=1, kh=1, kw=1, pad_t_front=0, pad_h=0, pad_w=0)).info()
+    assert pw.path == c3d.CONV3D_PATH_POINTWISE and pw.gemm_k == 512
+
+
+def test_forced_tile_and_unknown_tile():
+    os.environ["CONV3D_TILE"] = "m128n128k64s3w4"
+    try:
+        i = c3d.conv3d_plan(desc()).info()
+        assert (i.tile_m, i.tile_n, i.tile_k, i.stages) == (128, 128, 64, 3)
+        os.environ["CONV3D_TILE"] = "no-such-tile"
+        assert plan_status(desc()) == c3d.CONV3D_ERR_INVALID_ARG
+    finally:
+        del os.environ["CONV3D_TILE"]
+
+
+A = 0x7F0000000000  # fake, aligned, never dereferenced device addresses
+MB = 1 << 20
+
+
+def fwd(p, x=A, w=A + 512 * MB, b=A + 1024 * MB, r=None, y=A + 1536 * MB, ws=None, wsb=0):
+    lib = c3d.load_library()
+    return lib.conv3d_forward(p.handle, x, w, b, r, y, ws, wsb, None)
+
+
+def test_forward_argument_checks():
+    p = c3d.conv3d_plan(desc())
+    lib = c3d.load_library()
+    assert lib.conv3d_forward(None, A, A, A, None, A, None, 0, None) == c3d.CONV3D_ERR_INVALID_ARG
+    assert fwd(p, x=None) == c3d.CONV3D_ERR_INVALID_ARG
+    assert fwd(p, b=None) == c3d.CONV3D_ERR_INVALID_ARG           # plan has a bias
+    assert fwd(p, x=A + 2) == c3d.CONV3D_ERR_INVALID_ARG          # misaligned
+    assert fwd(p, y=A + 1024) == c3d.CONV3D_ERR_INVALID_ARG       # y overlaps x
+    pr = c3d.conv3d_plan(desc(flags=c3d.CONV3D_F_BIAS | c3d.CONV3D_F_RESIDUAL))
+    assert fwd(pr) == c3d.CONV3D_ERR_INVALID_ARG                  # residual missing
+    p1 = c3d.conv3d_plan(desc(t=1))
+    assert fwd(p1) == c3d.CONV3D_ERR_WORKSPACE
+    assert fwd(p1, ws=A + 2048 * MB, wsb=16) == c3d.CONV3D_ERR_WORKSPACE
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="host without a GPU only")
+def test_forward_without_a_device_reports_no_device():
+    p = c3d.conv3d_plan(desc())
+    assert fwd(p) == c3d.CONV3D_ERR_NO_DEVICE
+
+
+def test_groupnorm_argument_checks():
+    lib = c3d.load_library()
+    assert c3d.groupnorm_silu_workspace(1, 100, 256, 32) > 0
+    assert c3d.groupnorm_silu_workspace(1, 100, 256, 3) == 0
+    assert c3d.groupnorm_silu_workspace(1, 100, 96, 32) == 0   # 3 channels per group
+
+    def gn(x=A, y=A + 512 * MB, n=1, thw=100, c=256, g=32, eps=1e-6, ws=A + 1024 * MB, wsb=1 << 20):
+        return lib.groupnorm_silu(x, A + 1536 * MB, A + 1600 * MB, y, n, thw, c, g, eps, 1, ws,
+                                  wsb, None)
+    assert gn(x=None) == c3d.CONV3D_ERR_INVALID_ARG
+    assert gn(g=3) == c3d.CONV3D_ERR_INVALID_ARG
+    assert gn(c=96) == c3d.CONV3D_ERR_UNSUPPORTED
+    assert gn(eps=-1.0) == c3d.CONV3D_ERR_INVALID_ARG
+    assert gn(x=A + 8) == c3d.CONV3D_ERR_INVALID_ARG
+    assert gn(y=A + 1024) == c3d.CONV3D_ERR_INVALID_ARG           # partial overlap
+    assert gn(wsb=8) == c3d.CONV3D_ERR_WORKSPACE

@@ -282,3 +282,28 @@ def test_pins_catch_plausible_mistakes():
     }
     for name, y in mistakes.items():
         assert np.abs(y - ref).max() > 1e-3, name
+
+
+def test_f16_decoder_is_exact_for_every_bit_pattern():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_f64(int(b)) for b in bits])
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(np.isinf(got) & (got > 0), np.isinf(ref) & (ref > 0))
+    assert np.array_equal(np.signbit(got[finite]), np.signbit(ref[finite]))
+
+
+def test_points_read_fp16_inputs_in_place():
+    rng = np.random.default_rng(39)
+    x16 = rng.normal(size=(1, 3, 5, 4, 8)).astype(np.float16)
+    w = rnd((4, 3, 3, 3, 8), 40)
+    b = rnd((4,), 41)
+    r16 = rng.normal(size=(1, 3, 5, 4, 4)).astype(np.float16)
+    y, s = oracle.conv3d(x16.astype(np.float64), w, b, r16.astype(np.float64), (2, 0, 1, 1), R)
+    m = rng.integers(0, 60, 40)
+    co = rng.integers(0, 4, 40)
+    yp, sp = oracle.conv3d_points(x16, w, b, r16, (2, 0, 1, 1), R, m, co)
+    assert np.array_equal(yp, y.reshape(-1, 4)[m, co])
+    assert np.array_equal(sp, s.reshape(-1, 4)[m, co])

@@ -20,6 +20,8 @@ Layouts: activations NDHWC [N, T, H, W, C]; weights [Cout, kt, kh, kw, Cin].
 """
 from __future__ import annotations
 
+import concurrent.futures
+import os
 from dataclasses import dataclass, replace
 
 import numpy as np
@@ -85,53 +87,78 @@ def kaiming_bound(shape: ConvShape) -> float:
     return float(np.sqrt(6.0 / (shape.kt * shape.kh * shape.kw * shape.cin)))
 
 
-def _rngs(seed: int, count: int):
-    return [np.random.Generator(np.random.PCG64(s))
-            for s in np.random.SeedSequence(seed).spawn(count)]
+def _seeds(seed: int, count: int):
+    return np.random.SeedSequence(seed).spawn(count)
 
 
-def normal_f16(rng, shape, mean=0.0, std=1.0, chunk_elems=1 << 26):
-    """N(mean, std) drawn as float32 in sequential chunks, rounded once to fp16."""
+def _gen(ss):
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+CHUNK = 1 << 24  # elements per independently seeded chunk of an activation tensor
+
+
+def _fill_chunks(flat, ss, draw):
+    """Fill flat[k*CHUNK:(k+1)*CHUNK] from child seed k of ss, in a thread pool.
+
+    The values depend only on ss and the chunk index, never on the thread
+    count (numpy's Generator releases the GIL while it fills).
+    """
+    nchunks = (flat.size + CHUNK - 1) // CHUNK
+    kids = ss.spawn(nchunks)
+
+    def one(k):
+        s, e = k * CHUNK, min(flat.size, (k + 1) * CHUNK)
+        flat[s:e] = draw(_gen(kids[k]), s, e)
+
+    if nchunks == 1:
+        one(0)
+    else:
+        workers = min(nchunks, max(1, min(16, os.cpu_count() or 1)))
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, range(nchunks)))
+
+
+def normal_f16(ss, shape, mean=0.0, std=1.0, channel_scale=None):
+    """N(mean, std) drawn as float32, optionally scaled per channel (last axis), rounded once to fp16."""
     out = np.empty(shape, np.float16)
     flat = out.reshape(-1)
-    for s in range(0, flat.size, chunk_elems):
-        e = min(flat.size, s + chunk_elems)
-        v = rng.standard_normal(e - s, dtype=np.float32)
+    c = shape[-1]
+
+    def draw(g, s, e):
+        v = g.standard_normal(e - s, dtype=np.float32)
         if std != 1.0:
             v *= np.float32(std)
         if mean != 0.0:
             v += np.float32(mean)
-        flat[s:e] = v.astype(np.float16)
+        if channel_scale is not None:
+            # chunk starts are multiples of CHUNK, itself a multiple of c (c divides 2^24 here)
+            v.reshape(-1, c)[:, channel_scale[0]] *= np.float32(channel_scale[1])
+        return v.astype(np.float16)
+
+    if channel_scale is not None and CHUNK % c:
+        raise ValueError("channel count must divide the chunk size")
+    _fill_chunks(flat, ss, draw)
     return out
 
 
-def uniform_f16(rng, shape, bound):
-    return rng.uniform(-bound, bound, size=shape).astype(np.float16)
+def uniform_f16(ss, shape, bound):
+    return _gen(ss).uniform(-bound, bound, size=shape).astype(np.float16)
 
 
 def conv_inputs(shape: ConvShape, seed: int, w_bound=None, b_std=0.02, with_bias=True,
                 hot_channels=0, hot_scale=50.0):
     """x, w, b (fp16 numpy) for one conv.  ``hot_channels`` input channels x hot_scale."""
-    rx, rw, rb, rp = _rngs(seed, 4)
+    sx, sw, sb, sp = _seeds(seed, 4)
     if w_bound is None:
         w_bound = kaiming_bound(shape)
+    scale = None
     if hot_channels:
-        x = np.empty(shape.x_shape, np.float16)
-        hot = rp.permutation(shape.cin)[:hot_channels]
-        scale = np.ones(shape.cin, np.float32)
-        scale[hot] = np.float32(hot_scale)
-        xf = x.reshape(-1, shape.cin)
-        rows = xf.shape[0]
-        step = max(1, (1 << 25) // shape.cin)
-        for s in range(0, rows, step):
-            e = min(rows, s + step)
-            v = rx.standard_normal((e - s, shape.cin), dtype=np.float32)
-            v *= scale
-            xf[s:e] = v.astype(np.float16)
-    else:
-        x = normal_f16(rx, shape.x_shape)
-    w = uniform_f16(rw, shape.w_shape, w_bound)
-    b = normal_f16(rb, (shape.cout,), 0.0, b_std) if with_bias else None
+        hot = np.sort(_gen(sp).permutation(shape.cin)[:hot_channels])
+        scale = (hot, hot_scale)
+    x = normal_f16(sx, shape.x_shape, channel_scale=scale)
+    w = uniform_f16(sw, shape.w_shape, w_bound)
+    b = normal_f16(sb, (shape.cout,), 0.0, b_std) if with_bias else None
     return {"x": x, "w": w, "b": b}
 
 
@@ -146,9 +173,8 @@ def workload_inputs(k: int):
     if k == 2:
         return dict(shape=CAUSAL_256, **conv_inputs(CAUSAL_256, seed))
     if k == 3:
-        a, b2 = np.random.SeedSequence(seed).spawn(2)
-        st1 = conv_inputs(STAGE_3X3, int(a.generate_state(1)[0]), hot_channels=5)
-        st2 = conv_inputs(STAGE_1X1, int(b2.generate_state(1)[0]))
+        st1 = conv_inputs(STAGE_3X3, seed, hot_channels=5)
+        st2 = conv_inputs(STAGE_1X1, seed + 100)
         return {"shape": STAGE_3X3, "x": st1["x"], "w": st1["w"], "b": st1["b"],
                 "shape2": STAGE_1X1, "w2": st2["w"], "b2": st2["b"]}
     if k == 4:
@@ -158,7 +184,7 @@ def workload_inputs(k: int):
 
 def block_inputs(shape: ConvShape, seed: int):
     """Decoder-block tensors in the order x, gamma1, beta1, w1, b1, gamma2, beta2, w2, b2."""
-    r = _rngs(seed, 9)
+    r = _seeds(seed, 9)
     c = shape.cin
     bound = kaiming_bound(shape)
     return {
@@ -178,7 +204,7 @@ def block_inputs(shape: ConvShape, seed: int):
 
 
 def gn_inputs(n: int, thw_shape, c: int, seed: int, mean=0.0, std=1.0):
-    """x [n, *thw_shape, c], gamma ~ N(1, 0.1), beta ~ N(0, 0.1), all fp16."""
-    rx, rg, rb = _rngs(seed, 3)
-    x = normal_f16(rx, (n,) + tuple(thw_shape) + (c,), mean, std)
-    return {"x": x, "gamma": normal_f16(rg, (c,), 1.0, 0.1), "beta": normal_f16(rb, (c,), 0.0, 0.1)}
+    """x [n, *thw_shape, c] ~ N(mean, std), gamma ~ N(1, 0.1), beta ~ N(0, 0.1), all fp16."""
+    sx, sg, sb = _seeds(seed, 3)
+    x = normal_f16(sx, (n,) + tuple(thw_shape) + (c,), mean, std)
+    return {"x": x, "gamma": normal_f16(sg, (c,), 1.0, 0.1), "beta": normal_f16(sb, (c,), 0.0, 0.1)}
