@@ -186,7 +186,7 @@ def groupnorm_silu_workspace(n, thw, c, groups) -> int:
 
 def groupnorm_silu(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, workspace,
                    workspace_bytes=None, stream=None) -> None:
-    """Enqueue y = [SiLU](GroupNorm(x)) on ``stream``; workspace zero-filled before first use."""
+    """Enqueue y = [SiLU](GroupNorm(x)) on ``stream``."""
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().groupnorm_silu(_addr(x), _addr(gamma), _addr(beta), _addr(y), n, thw, c,

@@ -46,6 +46,11 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("kernel launch stubs missing from the host objects: %s" % missing[:3])
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

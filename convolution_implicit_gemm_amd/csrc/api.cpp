@@ -222,6 +222,17 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
         delete p;
         return fail(CONV3D_ERR_INVALID_ARG, "CONV3D_TILE=%s names no tile configuration", forced);
     }
+    q.in_vox = (int32_t)((int64_t)d->n * q.T * q.H * q.W);
+    const int64_t wbytes = (int64_t)q.Cout * q.K * 2;
+    if (wbytes >= ((int64_t)1 << 30)) {
+        delete p;
+        return fail(CONV3D_ERR_UNSUPPORTED, "weights of 1 GiB or more");
+    }
+    q.w_bytes = (uint32_t)wbytes;
+    if (c3d::tile_window_voxels(q, best->bm) * q.Cin * 2 >= ((int64_t)1 << 30)) {
+        delete p;
+        return fail(CONV3D_ERR_UNSUPPORTED, "one tile's input window would reach 1 GiB (frames too large)");
+    }
     p->tile = best;
     p->tail = (q.Cin % best->bk) != 0;
     q.cpt = (q.Cin + best->bk - 1) / best->bk;

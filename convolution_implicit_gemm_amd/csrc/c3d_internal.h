@@ -24,9 +24,15 @@ struct ConvParams {
     int32_t cpt;           // K-iterations per tap: ceil(Cin / BK)
     int32_t niter;         // kt*kh*kw*cpt
     int32_t m_tiles, n_tiles;
-    int64_t M;             // N*To*Ho*Wo
+    int32_t in_vox;        // N*T*H*W input voxels
+    uint32_t w_bytes;      // Cout*K*2, below 2^30
+    int64_t M;             // N*To*Ho*Wo, below 2^30
     int64_t tiles;         // m_tiles*n_tiles
 };
+
+// Largest input window, in voxels, that one tile of bm output rows can read
+// (the kernel addresses it through one buffer resource with 32-bit offsets).
+int64_t tile_window_voxels(const ConvParams &q, int bm);
 
 typedef hipError_t (*ConvLaunchFn)(const ConvParams &p, hipStream_t s);
 

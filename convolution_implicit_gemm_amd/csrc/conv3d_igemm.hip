@@ -17,16 +17,20 @@
 //    "B" operand the gathered activations (columns = voxels), so each lane's
 //    accumulators hold 4 consecutive output channels of one voxel: the
 //    epilogue writes NDHWC rows directly.
-//  * Global -> LDS with global_load_lds_dwordx4 (16 B per lane straight into
-//    LDS, no VGPR staging).  A load instruction fills 1 KiB of LDS linearly by
-//    lane, so the bank swizzle (16-byte chunk index XOR a function of the row)
-//    is applied on the global side: each lane fetches the chunk that belongs
-//    at its LDS slot.
-//  * Padding is resolved in address arithmetic once per tap: a lane whose
-//    source voxel lies outside H/W (or outside T with zero temporal padding)
-//    reads a 16-byte zero line instead; replicate temporal padding clamps the
-//    frame index.  Rows past M, channels past Cout and (on the tail variant)
-//    channels past Cin read the same zero line.
+//  * Global -> LDS with buffer_load_dwordx4 ... lds (16 B per lane straight
+//    into LDS, no VGPR staging).  A load instruction fills 1 KiB of LDS
+//    linearly by lane, so the bank swizzle (16-byte chunk index XOR a function
+//    of the row) is applied on the global side: each lane fetches the chunk
+//    that belongs at its LDS slot.
+//  * Padding is resolved in address arithmetic, per tap: a lane whose source
+//    voxel lies outside H/W (or outside T with zero temporal padding) gets an
+//    offset past the buffer's record count, and the buffer unit's range check
+//    then writes zeros into LDS; replicate temporal padding clamps the frame
+//    index.  Rows past M, channels past Cout and (tail variant) channels past
+//    Cin use the same out-of-range offset.  Each tile addresses its own window
+//    of the input (a buffer resource based at the lowest voxel it can touch),
+//    so 32-bit offsets suffice for multi-GB tensors.  Walking along K inside a
+//    tap only moves the scalar offset.
 //  * STAGES-deep ring of LDS buffers; one s_waitcnt vmcnt(N) + s_barrier per
 //    K-iteration.  __syncthreads() is avoided on purpose: its release fence
 //    waits for every outstanding load, which would drain the prefetch ring.
@@ -42,8 +46,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Read by every padded tap, out-of-range row and channel tail.  Never written.
-__device__ __attribute__((aligned(256))) uint32_t g_zero_line[64];
+// 1: pin the MFMA / LDS-read / load interleave with sched_group_barrier.
+#ifndef C3D_SCHED
+#define C3D_SCHED 0
+#endif
 
 // Bank swizzle of 16-byte chunks within an LDS row of BK halves.  Chosen so
 // that 32 consecutive rows read at one logical chunk by ds_read_b128 hit
@@ -59,11 +65,52 @@ __device__ __forceinline__ int swz(int row) {
     }
 }
 
+// Wait until at most N global->LDS loads of this wave are in flight and all of
+// its LDS reads have returned, then meet the other waves.  Loads retire in
+// order, so "at most N" means every older stage has landed.
 template <int N>
-__device__ __forceinline__ void wait_loads_and_barrier() {
+__device__ __forceinline__ void wait_lds_and_loads() {
     static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+
+// Buffer resources: the device pass uses the gfx950 128-bit descriptor type;
+// the host pass (which never runs these functions) sees a placeholder.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+#else
+struct buf_rsrc {
+    uint32_t w[4];
+};
+#endif
+
+// Raw (unswizzled, stride 0) buffer over `bytes` bytes at `base`.  Loads whose
+// voffset + soffset reach past `bytes` return zeros, dword by dword.
+__device__ __forceinline__ buf_rsrc make_rsrc(const void *base, uint32_t bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+#else
+    (void)base;
+    (void)bytes;
+    return buf_rsrc{};
+#endif
+}
+
+// 16 bytes per lane from base + voff + soff straight into LDS: lane i writes
+// lds + 16*i (lds must be wave-uniform).  Only the device pass sees the builtin.
+__device__ __forceinline__ void dma16(buf_rsrc r, char *lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
+#else
+    (void)r;
+    (void)lds;
+    (void)voff;
+    (void)soff;
+#endif
+}
+
+// Offset that is always past a buffer's record count (records stay below 2^30).
+constexpr uint32_t kOOB = 0x80000000u;
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool TAIL>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kernel(ConvParams p) {
@@ -78,9 +125,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
     constexpr int B_OFF = BN * RB;                  // activations follow the weights
     constexpr int STAGE_BYTES = (BM + BN) * RB;
     static_assert(BM % RPI == 0 && BN % RPI == 0, "tile rows must fill whole load instructions");
-    static_assert(STAGES == 2 || (QA % NW == 0 && QB % NW == 0),
-                  "a deep ring needs the same load count on every wave");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS is 160 KiB per CU");
+    static_assert(KS >= 2, "two k-steps per stage at least");
 
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
 
@@ -88,117 +134,143 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     // XCD-aware renumbering: XCD x = blockIdx mod 8 gets a contiguous tile range.
-    const int64_t nblk = p.tiles;
-    const int64_t bid = blockIdx.x;
-    const int64_t per = nblk >> 3, rem = nblk & 7;
-    const int xcd = (int)(bid & 7);
-    const int64_t tile = xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3);
-    const int mt = (int)(tile / p.n_tiles), nt = (int)(tile - (int64_t)mt * p.n_tiles);
-    const int64_t m0 = (int64_t)mt * BM;
+    const int nblk = (int)p.tiles;
+    const int bid = blockIdx.x;
+    const int per = nblk >> 3, rem = nblk & 7;
+    const int xcd = bid & 7;
+    const int tile = xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3);
+    const int mt = tile / p.n_tiles, nt = tile - mt * p.n_tiles;
+    const int m0 = mt * BM;
     const int n0 = nt * BN;
 
     const int T = p.T, H = p.H, W = p.W, Cin = p.Cin;
     const int HW = H * W;
+    const int M = (int)p.M;
+
+    // input voxel index of an output coordinate, in input strides (may lie
+    // outside the input when padding exceeds half the kernel; only offsets
+    // derived from it and range-checked are ever used)
+    auto vb_of = [&](int m, int &to, int &ho, int &wo) {
+        wo = m % p.Wo;
+        const int r1 = m / p.Wo;
+        ho = r1 % p.Ho;
+        const int r2 = r1 / p.Ho;
+        to = r2 % p.To;
+        const int n = r2 / p.To;
+        return ((n * T + to) * H + ho) * W + wo;
+    };
+
+    // this tile's window of input voxels: [lo, hi)
+    int lo, hi;
+    {
+        int t_, h_, w_;
+        const int m_last = (m0 + BM < M ? m0 + BM : M) - 1;
+        lo = vb_of(m0, t_, h_, w_) - (p.ptf * HW + p.ph * W + p.pw);
+        lo = lo < 0 ? 0 : lo;
+        hi = vb_of(m_last, t_, h_, w_) + (p.kt - 1) * HW + (p.kh - 1) * W + (p.kw - 1) + 1;
+        hi = hi > p.in_vox ? p.in_vox : hi;
+        if (hi < lo) hi = lo;
+    }
+    const buf_rsrc xr = make_rsrc(p.x + (int64_t)lo * Cin, (uint32_t)(hi - lo) * (uint32_t)Cin * 2u);
+    const buf_rsrc wr = make_rsrc(p.w, p.w_bytes);
 
     // ---- per-lane gather slots: one output row per activation load instruction
     const int lrow = lane / CPR, lchunk = lane % CPR;
-    int a_vb[LA], a_t[LA], a_h[LA], a_w[LA], a_c8[LA];
+    const int cin2 = Cin * 2;
+    int a_t[LA], a_h[LA], a_w[LA], a_base[LA], a_c2[LA];
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
         const int row = (j * NW + wv) * RPI + lrow;
-        a_c8[j] = (lchunk ^ swz<BK>(row)) * 8;
-        const int64_t m = m0 + row;
-        if (m < p.M) {
-            const int wo = (int)(m % p.Wo);
-            const int64_t r1 = m / p.Wo;
-            const int ho = (int)(r1 % p.Ho);
-            const int64_t r2 = r1 / p.Ho;
-            const int to = (int)(r2 % p.To);
-            const int n = (int)(r2 / p.To);
+        a_c2[j] = (lchunk ^ swz<BK>(row)) * 16;  // byte offset of this lane's chunk
+        const int m = m0 + row;
+        if (m < M) {
+            int to, ho, wo;
+            const int vb = vb_of(m, to, ho, wo);
             a_t[j] = to;
             a_h[j] = ho;
             a_w[j] = wo;
-            a_vb[j] = ((n * T + to) * H + ho) * W + wo;
+            a_base[j] = vb - lo - to * HW;  // + ts*HW + tap offset = source voxel - lo
         } else {
             a_t[j] = 0;
             a_h[j] = 1 << 20;  // never inside [0, H): the row reads zeros
             a_w[j] = 0;
-            a_vb[j] = 0;
+            a_base[j] = 0;
         }
     }
-    const char *b_ptr[LB];
+    uint32_t b_voff[LB];
+    int b_c8[LB];
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
         const int row = (j * NW + wv) * RPI + lrow;
         const int co = n0 + row;
-        const int c8 = (lchunk ^ swz<BK>(row)) * 8;
-        b_ptr[j] = co < p.Cout ? reinterpret_cast<const char *>(p.w + (int64_t)co * p.K + c8) : nullptr;
+        b_c8[j] = (lchunk ^ swz<BK>(row)) * 8;
+        b_voff[j] = co < p.Cout ? (uint32_t)(co * p.K + b_c8[j]) * 2u : kOOB;
     }
-    int b_c8[LB];
-#pragma unroll
-    for (int j = 0; j < LB; ++j) b_c8[j] = (lchunk ^ swz<BK>((j * NW + wv) * RPI + lrow)) * 8;
 
-    const char *a_ptr[LA];
-    auto set_tap = [&](int tau, int r, int s) {
+    // ---- load side: the stage being fetched is (tap = (tau, r, s), ci0).  Its
+    // per-lane offsets are recomputed branch-free every K-iteration (a few VALU
+    // per slot, interleaved with the MFMAs); K inside a tap moves only the
+    // scalar offset.  After the last stage the state freezes, so the extra
+    // fetches that keep every wave's load count constant re-read valid data
+    // into a buffer nobody reads again.
+    const int niter = p.niter;
+    const int t_lo = p.replicate ? 0 : -(1 << 20), t_hi = p.replicate ? T - 1 : (1 << 20);
+    int ld_it = 0, ld_ci = 0, ld_tap = 0, ld_tau = 0, ld_r = 0, ld_s = 0;
+    uint32_t a_voff[LA];
+    auto set_offsets = [&]() {
+        const int dr = ld_r - p.ph, ds = ld_s - p.pw;
+        const int dt = ld_tau - p.ptf;
+        const int rs = dr * W + ds;
 #pragma unroll
         for (int j = 0; j < LA; ++j) {
-            int ts = a_t[j] + tau - p.ptf;
-            bool ok;
-            if (p.replicate) {
-                ts = ts < 0 ? 0 : (ts > T - 1 ? T - 1 : ts);
-                ok = true;
-            } else {
-                ok = (unsigned)ts < (unsigned)T;
-            }
-            const int hs = a_h[j] + r - p.ph, ws = a_w[j] + s - p.pw;
-            ok = ok && (unsigned)hs < (unsigned)H && (unsigned)ws < (unsigned)W;
-            const int vox = a_vb[j] + (ts - a_t[j]) * HW + (r - p.ph) * W + (s - p.pw);
-            a_ptr[j] = ok ? reinterpret_cast<const char *>(p.x + (int64_t)vox * Cin + a_c8[j]) : nullptr;
+            int ts = a_t[j] + dt;
+            ts = ts < t_lo ? t_lo : (ts > t_hi ? t_hi : ts);  // clamp only when replicating
+            const bool ok = ((unsigned)ts < (unsigned)T) & ((unsigned)(a_h[j] + dr) < (unsigned)H) &
+                            ((unsigned)(a_w[j] + ds) < (unsigned)W);
+            const int rel = a_base[j] + ts * HW + rs;
+            // valid offsets are below 2^30 (the plan bounds every tile's window);
+            // invalid ones land in [2^31, 2^31 + 2^30): past the records, and
+            // far enough from 2^32 that adding the scalar offset cannot wrap.
+            // Arithmetic rather than a select, which the compiler would turn
+            // into an exec-masked block around the multiply.
+            a_voff[j] = (((uint32_t)rel * (uint32_t)cin2 + (uint32_t)a_c2[j]) & 0x3FFFFFFFu) |
+                        ((uint32_t)!ok << 31);
         }
     };
-
-    const char *zero = reinterpret_cast<const char *>(g_zero_line);
-    auto issue = [&](int stage, int tap, int ci0) {
-        char *sb = smem + stage * STAGE_BYTES;
-        const int64_t kofs = ((int64_t)tap * Cin + ci0) * 2;
+    auto fire = [&](int buf) {
+        char *sb = smem + buf * STAGE_BYTES;
+        const uint32_t s_w = (uint32_t)(ld_tap * Cin + ld_ci) * 2u;
+        const uint32_t s_a = (uint32_t)ld_ci * 2u;
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
             const int q = j * NW + wv;
             if (QB % NW == 0 || q < QB) {
-                const bool ok = b_ptr[j] != nullptr && (!TAIL || ci0 + b_c8[j] < Cin);
-                const char *src = ok ? b_ptr[j] + kofs : zero;
-                __builtin_amdgcn_global_load_lds(src, (lds_void *)(sb + q * 1024), 16, 0, 0);
+                const uint32_t v = (!TAIL || ld_ci + b_c8[j] < Cin) ? b_voff[j] : kOOB;
+                dma16(wr, sb + q * 1024, v, s_w);
             }
         }
 #pragma unroll
         for (int j = 0; j < LA; ++j) {
             const int q = j * NW + wv;
             if (QA % NW == 0 || q < QA) {
-                const bool ok = a_ptr[j] != nullptr && (!TAIL || ci0 + a_c8[j] < Cin);
-                const char *src = ok ? a_ptr[j] + ci0 * 2 : zero;
-                __builtin_amdgcn_global_load_lds(src, (lds_void *)(sb + B_OFF + q * 1024), 16, 0, 0);
+                const uint32_t v = (!TAIL || ld_ci + a_c2[j] / 2 < Cin) ? a_voff[j] : kOOB;
+                dma16(xr, sb + B_OFF + q * 1024, v, s_a);
             }
         }
-    };
-
-    // ---- load-side iteration state (runs STAGES-1 iterations ahead)
-    int ld_it = 0, ld_ci = 0, ld_tap = 0, ld_tau = 0, ld_r = 0, ld_s = 0;
-    set_tap(0, 0, 0);
-    auto advance = [&]() {
+        // advance (tau, r, s, ci0) with selects only; freeze after the last stage
+        const int step = ld_it + 1 < niter ? 1 : 0;
         ++ld_it;
-        ld_ci += BK;
-        if (ld_ci >= Cin) {
-            ld_ci = 0;
-            ++ld_tap;
-            if (++ld_s == p.kw) {
-                ld_s = 0;
-                if (++ld_r == p.kh) {
-                    ld_r = 0;
-                    ++ld_tau;
-                }
-            }
-            if (ld_it < p.niter) set_tap(ld_tau, ld_r, ld_s);
-        }
+        const int nci = ld_ci + BK * step;
+        const int wrap = nci >= Cin ? 1 : 0;
+        ld_ci = wrap ? 0 : nci;
+        ld_tap += wrap;
+        const int ns = ld_s + wrap;
+        const int wrap_s = ns == p.kw ? 1 : 0;
+        ld_s = wrap_s ? 0 : ns;
+        const int nr = ld_r + wrap_s;
+        const int wrap_r = nr == p.kh ? 1 : 0;
+        ld_r = wrap_r ? 0 : nr;
+        ld_tau += wrap_r;
     };
 
     // ---- per-lane LDS read offsets for the MFMA fragments
@@ -218,65 +290,69 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    constexpr int LOADS = LA + LB;  // per wave per stage (uniform when STAGES > 2)
-    const int niter = p.niter;
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) {
-        if (ld_it < niter) {
-            issue(s, ld_tap, ld_ci);
-            advance();
-        }
-    }
-
-    for (int it = 0; it < niter; ++it) {
-        if (it + STAGES - 2 < niter)
-            wait_loads_and_barrier<(STAGES - 2) * LOADS>();
-        else
-            wait_loads_and_barrier<0>();
-        if (ld_it < niter) {
-            issue(ld_it % STAGES, ld_tap, ld_ci);
-            advance();
-        }
-        const char *sb = smem + (it % STAGES) * STAGE_BYTES;
-        // Fragments of k-step kk+1 are read while the MFMAs of kk issue.
-        half8_t af[2][TN], bf[2][TM];
+    half8_t af[2][TN], bf[2][TM];
+    auto read_frags = [&](const char *sb, int kk, int slot) {
 #pragma unroll
         for (int i = 0; i < TN; ++i)
-            af[0][i] = *reinterpret_cast<const half8_t *>(sb + a_frag0 + i * 32 * RB + koff[0]);
+            af[slot][i] = *reinterpret_cast<const half8_t *>(sb + a_frag0 + i * 32 * RB + koff[kk]);
 #pragma unroll
         for (int j = 0; j < TM; ++j)
-            bf[0][j] = *reinterpret_cast<const half8_t *>(sb + b_frag0 + j * 32 * RB + koff[0]);
+            bf[slot][j] = *reinterpret_cast<const half8_t *>(sb + b_frag0 + j * 32 * RB + koff[kk]);
+    };
+    auto mfmas = [&](int slot) {
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const int cur = kk & 1, nxt = cur ^ 1;
-            if (kk + 1 < KS) {
+        for (int i = 0; i < TN; ++i)
 #pragma unroll
-                for (int i = 0; i < TN; ++i)
-                    af[nxt][i] = *reinterpret_cast<const half8_t *>(sb + a_frag0 + i * 32 * RB + koff[kk + 1]);
+            for (int j = 0; j < TM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[slot][i], bf[slot][j], acc[i][j], 0, 0, 0);
+    };
+
+    // Loads per wave per stage.  Waves may differ by one instruction when a
+    // tile's rows do not split evenly over the waves; waiting for "at most
+    // STAGES-1 stages of the smallest count" in flight still guarantees, on
+    // every wave, that its oldest stage has landed.
+    constexpr int LOADS = QA / NW + QB / NW;
+    constexpr int READS = TN + TM, MF = TN * TM;
+
+    // prologue: fill every buffer, wait for stage 0, read its first k-step
 #pragma unroll
-                for (int j = 0; j < TM; ++j)
-                    bf[nxt][j] = *reinterpret_cast<const half8_t *>(sb + b_frag0 + j * 32 * RB + koff[kk + 1]);
-            }
-#pragma unroll
-            for (int i = 0; i < TN; ++i)
-#pragma unroll
-                for (int j = 0; j < TM; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][i], bf[cur][j], acc[i][j], 0, 0, 0);
-        }
-        // Schedule: the first k-step's reads, then the remaining reads spread
-        // evenly between MFMAs, so the matrix pipe never waits on LDS.
-        constexpr int READS = TN + TM, MFMAS = TN * TM;
-        constexpr int PF_READS = (KS - 1) * READS;            // prefetched reads
-        constexpr int PF_MFMAS = (KS - 1) * MFMAS;            // MFMAs they hide behind
-        constexpr int GAP = PF_READS ? (PF_MFMAS / PF_READS > 0 ? PF_MFMAS / PF_READS : 1) : 1;
-        __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
-#pragma unroll
-        for (int q = 0; q < PF_READS; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, GAP, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, KS * MFMAS - GAP * PF_READS, 0);
+    for (int s = 0; s < STAGES; ++s) {
+        set_offsets();
+        fire(s);
     }
+    wait_lds_and_loads<(STAGES - 1) * LOADS>();
+    read_frags(smem, 0, 0);
+
+    for (int it = 0; it < niter; ++it) {
+        const int buf = it % STAGES;
+        const char *sb = smem + buf * STAGE_BYTES;
+        // region A: k-steps 0..KS-2 of this stage; offsets of the next fetch
+#pragma unroll
+        for (int kk = 0; kk < KS - 1; ++kk) {
+            read_frags(sb, kk + 1, (kk + 1) & 1);
+            mfmas(kk & 1);
+        }
+        set_offsets();
+        if constexpr (C3D_SCHED) {
+            constexpr int NM = (KS - 1) * MF, ND = (KS - 1) * READS;
+            constexpr int GAP = NM / ND > 0 ? NM / ND : 1;
+#pragma unroll
+            for (int q = 0; q < NM; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
+                if (q % GAP == 0 && q / GAP < ND)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);      // a few VALU
+            }
+        }
+        // stage it+1 has landed and every wave is done reading stage it
+        wait_lds_and_loads<(STAGES - 2) * LOADS>();
+        // region B: refill this stage's buffer, read k-step 0 of the next stage,
+        // and run the last k-step of this one meanwhile
+        fire(buf);
+        read_frags(smem + ((it + 1) % STAGES) * STAGE_BYTES, 0, 0);
+        mfmas((KS - 1) & 1);
+    }
+    wait_lds_and_loads<0>();  // drain the extra fetches before LDS is released
 
     // ---- epilogue: + bias (+ residual) in fp32, one RNE rounding, NDHWC store.
     // Lane holds, for sub-tile (i, j) and register 4g+e: channel
@@ -295,9 +371,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
             }
 #pragma unroll
             for (int j = 0; j < TM; ++j) {
-                const int64_t m = m0 + wmi * WM + j * 32 + rrow;
-                if (m >= p.M) continue;
-                const int64_t o = m * p.Cout + co;
+                const int m = m0 + wmi * WM + j * 32 + rrow;
+                if (m >= M) continue;
+                const int64_t o = (int64_t)m * p.Cout + co;
                 f32x4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] + bv[e];
@@ -336,6 +412,20 @@ static const TileCfg k_tiles[] = {
     C3D_TILE("m128n64k64s2w4", 128, 64, 64, 32, 64, 2),
     C3D_TILE("m128n32k32s2w4", 128, 32, 32, 32, 32, 2),
 };
+
+int64_t tile_window_voxels(const ConvParams &q, int bm) {
+    // bm consecutive output rows cross at most this many output rows, frames
+    // and samples; each crossing can skip input voxels the output does not map.
+    const int64_t rows = (bm - 1) / q.Wo + 1;
+    const int64_t frames = (bm - 1) / ((int64_t)q.Ho * q.Wo) + 1;
+    const int64_t samples = (bm - 1) / ((int64_t)q.To * q.Ho * q.Wo) + 1;
+    const int64_t HW = (int64_t)q.H * q.W;
+    const int64_t skip = rows * (q.W > q.Wo ? q.W - q.Wo : 0) + frames * (q.H > q.Ho ? q.H - q.Ho : 0) * q.W +
+                         samples * (q.T > q.To ? q.T - q.To : 0) * HW;
+    const int64_t halo = (int64_t)q.ptf * HW + (int64_t)q.ph * q.W + q.pw + (int64_t)(q.kt - 1) * HW +
+                         (int64_t)(q.kh - 1) * q.W + (q.kw - 1) + 1;
+    return (bm - 1) + skip + halo;
+}
 
 const TileCfg *tile_table(int *count) {
     *count = (int)(sizeof(k_tiles) / sizeof(k_tiles[0]));

@@ -10,10 +10,11 @@
 //          one group and accumulates in registers with the shifted-data
 //          method (sums of x-K and (x-K)^2 about its first value K, fp32),
 //          then the block merges threads of a group (Chan's pairwise
-//          update) and writes (count, mean, M2) partials.  The last block to
-//          finish (device-scope counter) merges the SB partials of each
-//          (sample, group) with one wavefront per pair, and writes
-//          per-channel scale a = gamma*rstd and shift b = beta - mean*a.
+//          update) and writes (count, mean, M2) partials.
+//  final:  grid (G, N), one block per (sample, group): every thread loads its
+//          share of the SB partials at once, merges them, and the block
+//          reduces (shuffles, then LDS) to the group's mean and rstd; it
+//          writes per-channel scale a = gamma*rstd and shift b = beta - mean*a.
 //  apply:  grid (AB, N).  Each thread owns one channel vector, keeps its 8
 //          scales/shifts in registers, and streams y = x*a + b, then
 //          y*sigmoid(y), rounded once to fp16.
@@ -50,18 +51,17 @@ GnGeom gn_geom(int32_t n, int64_t thw, int32_t c) {
     int64_t maxb = (thw + 4 * vox_per_pass - 1) / (4 * vox_per_pass);
     g.sb = (int)(want < maxb ? want : maxb);
     if (g.sb < 1) g.sb = 1;
-    int64_t wanta = (4096 + n - 1) / n;
-    int64_t maxa = (thw + 2 * vox_per_pass - 1) / (2 * vox_per_pass);
+    int64_t wanta = (2048 + n - 1) / n;
+    int64_t maxa = (thw + 4 * vox_per_pass - 1) / (4 * vox_per_pass);
     g.ab = (int)(wanta < maxa ? wanta : maxa);
     if (g.ab < 1) g.ab = 1;
     return g;
 }
 
-// Workspace layout (bytes): [0,256) counter; then scale/shift [N][C] float x2;
-// then partials [N][SB][G] float4 (count, mean, M2, unused).
-size_t off_scale() { return 256; }
+// Workspace layout (bytes): scale/shift [N][C] float x2 from 0; then
+// partials [N][SB][G] float4 (count, mean, M2, unused), 256-byte aligned.
 size_t off_part(int32_t n, int32_t c) {
-    size_t b = 256 + (size_t)n * c * 2 * sizeof(float);
+    size_t b = (size_t)n * c * 2 * sizeof(float);
     return (b + 255) & ~(size_t)255;
 }
 
@@ -81,12 +81,10 @@ __device__ __forceinline__ Welford chan_merge(Welford a, Welford b) {
     return r;
 }
 
-__global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(
-    const _Float16 *__restrict__ x, int64_t thw, int32_t c, int32_t groups, int32_t sb, float eps,
-    const _Float16 *__restrict__ gamma, const _Float16 *__restrict__ beta, unsigned *counter,
-    float *__restrict__ scale, float *__restrict__ shift, float4 *__restrict__ part) {
+__global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(const _Float16 *__restrict__ x, int64_t thw,
+                                                                int32_t c, int32_t groups, int32_t sb,
+                                                                float4 *__restrict__ part) {
     __shared__ float4 red[kMaxThreads];
-    __shared__ bool am_last;
     const int n = blockIdx.y;
     const int b = blockIdx.x;
     const int vpv = c / 8;
@@ -152,48 +150,58 @@ __global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(
         }
         part[((size_t)n * sb + b) * groups + g] = make_float4(acc.n, acc.mean, acc.m2, 0.0f);
     }
+}
 
-    // last block merges everything
-    __threadfence();
+constexpr int kFinalThreads = 256;
+
+__global__ __launch_bounds__(kFinalThreads) void gn_final_kernel(const float4 *__restrict__ part, int32_t sb,
+                                                                 int32_t c, int32_t groups, float eps,
+                                                                 const _Float16 *__restrict__ gamma,
+                                                                 const _Float16 *__restrict__ beta,
+                                                                 float *__restrict__ scale,
+                                                                 float *__restrict__ shift) {
+    __shared__ float4 red[kFinalThreads / 64];
+    __shared__ float2 stat;
+    const int g = blockIdx.x, n = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float4 *p = part + (size_t)n * sb * groups + g;
+    Welford acc = {0.0f, 0.0f, 0.0f};
+    int b = tid;
+    // eight independent loads in flight per thread
+    for (; b + 7 * kFinalThreads < sb; b += 8 * kFinalThreads) {
+        float4 e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) e[u] = p[(size_t)(b + u * kFinalThreads) * groups];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc = chan_merge(acc, Welford{e[u].x, e[u].y, e[u].z});
+    }
+    for (; b < sb; b += kFinalThreads) {
+        const float4 e = p[(size_t)b * groups];
+        acc = chan_merge(acc, Welford{e.x, e.y, e.z});
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        Welford o;
+        o.n = __shfl_xor(acc.n, off);
+        o.mean = __shfl_xor(acc.mean, off);
+        o.m2 = __shfl_xor(acc.m2, off);
+        acc = chan_merge(acc, o);
+    }
+    if (lane == 0) red[wave] = make_float4(acc.n, acc.mean, acc.m2, 0.0f);
     __syncthreads();
     if (tid == 0) {
-        const unsigned total = gridDim.x * gridDim.y;
-        am_last = atomicAdd(counter, 1u) == total - 1;
+        Welford t = {0.0f, 0.0f, 0.0f};
+        for (int w = 0; w < kFinalThreads / 64; ++w) t = chan_merge(t, Welford{red[w].x, red[w].y, red[w].z});
+        stat = make_float2(t.mean, 1.0f / sqrtf(t.m2 / t.n + eps));
     }
     __syncthreads();
-    if (!am_last) return;
-    __threadfence();
-
-    // only full wavefronts take part: the merge below shuffles across all 64 lanes
-    const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
-    const int pairs = gridDim.y * groups;
-    for (int pidx = wave; wave < nwaves && pidx < pairs; pidx += nwaves) {
-        const int pn = pidx / groups, pg = pidx % groups;
-        Welford acc = {0.0f, 0.0f, 0.0f};
-        // plain loads: the device-scope fence above invalidated this CU's L1
-        for (int bb = lane; bb < sb; bb += 64) {
-            const float4 e = part[((size_t)pn * sb + bb) * groups + pg];
-            acc = chan_merge(acc, Welford{e.x, e.y, e.z});
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            Welford o;
-            o.n = __shfl_xor(acc.n, off);
-            o.mean = __shfl_xor(acc.mean, off);
-            o.m2 = __shfl_xor(acc.m2, off);
-            acc = chan_merge(acc, o);
-        }
-        const float var = acc.m2 / acc.n;
-        const float rstd = 1.0f / sqrtf(var + eps);
-        const int cg = c / groups;
-        for (int cc = lane; cc < cg; cc += 64) {
-            const int ch = pg * cg + cc;
-            const float a = rstd * (float)gamma[ch];
-            scale[(size_t)pn * c + ch] = a;
-            shift[(size_t)pn * c + ch] = (float)beta[ch] - acc.mean * a;
-        }
+    const int cg = c / groups;
+    for (int cc = tid; cc < cg; cc += kFinalThreads) {
+        const int ch = g * cg + cc;
+        const float a = stat.y * (float)gamma[ch];
+        scale[(size_t)n * c + ch] = a;
+        shift[(size_t)n * c + ch] = (float)beta[ch] - stat.x * a;
     }
-    if (tid == 0) *counter = 0u;  // ready for the next call on this workspace
 }
 
 __device__ __forceinline__ float silu_f32(float y) {
@@ -221,23 +229,22 @@ __global__ __launch_bounds__(kMaxThreads) void gn_apply_kernel(const _Float16 *_
     const half8_t *xs = reinterpret_cast<const half8_t *>(x + (size_t)n * thw * c);
     half8_t *ys = reinterpret_cast<half8_t *>(y + (size_t)n * thw * c);
     int64_t v = (int64_t)blockIdx.x * (blockDim.x / vpv) + tid / vpv;
-    for (; v + vox_step < thw; v += 2 * vox_step) {
-        const half8_t h0 = __builtin_nontemporal_load(xs + v * vpv + vi);
-        const half8_t h1 = __builtin_nontemporal_load(xs + (v + vox_step) * vpv + vi);
-        half8_t o0, o1;
+    // four 16-byte loads in flight per thread
+    for (; v + 3 * vox_step < thw; v += 4 * vox_step) {
+        half8_t h[4];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            float t0 = fmaf((float)h0[q], a[q], bsh[q]);
-            float t1 = fmaf((float)h1[q], a[q], bsh[q]);
-            if (SILU) {
-                t0 = silu_f32(t0);
-                t1 = silu_f32(t1);
+        for (int u = 0; u < 4; ++u) h[u] = __builtin_nontemporal_load(xs + (v + u * vox_step) * vpv + vi);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            half8_t o;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                float t = fmaf((float)h[u][q], a[q], bsh[q]);
+                if (SILU) t = silu_f32(t);
+                o[q] = (_Float16)t;
             }
-            o0[q] = (_Float16)t0;
-            o1[q] = (_Float16)t1;
+            __builtin_nontemporal_store(o, ys + (v + u * vox_step) * vpv + vi);
         }
-        __builtin_nontemporal_store(o0, ys + v * vpv + vi);
-        __builtin_nontemporal_store(o1, ys + (v + vox_step) * vpv + vi);
     }
     for (; v < thw; v += vox_step) {
         const half8_t h0 = __builtin_nontemporal_load(xs + v * vpv + vi);
@@ -264,13 +271,15 @@ hipError_t launch_groupnorm_silu(const _Float16 *x, const _Float16 *gamma, const
                                  void *ws, hipStream_t s) {
     const GnGeom g = gn_geom(n, thw, c);
     char *base = static_cast<char *>(ws);
-    unsigned *counter = reinterpret_cast<unsigned *>(base);
-    float *scale = reinterpret_cast<float *>(base + off_scale());
+    float *scale = reinterpret_cast<float *>(base);
     float *shift = scale + (size_t)n * c;
     float4 *part = reinterpret_cast<float4 *>(base + off_part(n, c));
-    hipLaunchKernelGGL(gn_stats_kernel, dim3(g.sb, n), dim3(g.threads), 0, s, x, thw, c, groups, g.sb, eps,
-                       gamma, beta, counter, scale, shift, part);
+    hipLaunchKernelGGL(gn_stats_kernel, dim3(g.sb, n), dim3(g.threads), 0, s, x, thw, c, groups, g.sb, part);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gn_final_kernel, dim3(groups, n), dim3(kFinalThreads), 0, s, part, g.sb, c, groups, eps,
+                       gamma, beta, scale, shift);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (silu)
         hipLaunchKernelGGL(gn_apply_kernel<true>, dim3(g.ab, n), dim3(g.threads), 0, s, x, y, thw, c, scale,

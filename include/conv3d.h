@@ -110,7 +110,8 @@ typedef struct {
  * too-large padding (a pad must be smaller than its kernel extent), an empty
  * output, or an unknown t_pad_mode / flag bit; UNSUPPORTED for c_in or c_out
  * not a multiple of 8, kernel extents above 7, spatial extents above 8192,
- * or 2^30 or more input or output voxels.
+ * 2^30 or more input or output voxels, weights of 1 GiB or more, or frames
+ * so large that the input rows one output tile reads span 1 GiB.
  * The environment variable CONV3D_FORCE_PATH=general behaves like
  * CONV3D_F_NO_T1_FASTPATH; CONV3D_TILE=<name> forces a tile configuration.
  */
@@ -145,9 +146,10 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
  * yhat = (x-mean)*rsqrt(var+eps)*gamma + beta, and y = yhat*sigmoid(yhat) if
  * apply_silu else yhat, rounded once to fp16.  y may equal x (in place).
  * groupnorm_silu_workspace() gives the workspace bytes (fp32 partial
- * statistics and per-channel scale/shift; it also holds a counter that each
- * call leaves at zero, so a workspace must be zero-filled once before its
- * first use and must not be shared by calls that may run concurrently).
+ * statistics and per-channel scale/shift); its contents are scratch,
+ * overwritten by each call, so calls that may run concurrently must not
+ * share one.  groupnorm_silu_workspace() returns 0 for arguments that
+ * groupnorm_silu would reject.
  * Errors: INVALID_ARG (null/misaligned pointers, non-positive sizes,
  * c % groups != 0, eps < 0), UNSUPPORTED ((c/groups) % 8 != 0, or c > 8192),
  * WORKSPACE, HIP.
