@@ -88,6 +88,7 @@ double tile_efficiency(const c3d::TileCfg &t) {
 struct conv3d_plan_s {
     conv3d_desc d;
     int path;
+    bool streaming;       // CONV3D_PATH_POINTWISE through the dedicated streaming kernel
     c3d::ConvParams prm;  // pointers filled per call
     const c3d::TileCfg *tile;
     bool tail;
@@ -241,6 +242,8 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
     q.n_tiles = (q.Cout + best->bn - 1) / best->bn;
     q.tiles = (int64_t)q.m_tiles * q.n_tiles;
     p->flops = 2.0 * (double)q.M * q.Cout * q.K;
+    p->streaming = path == CONV3D_PATH_POINTWISE && c3d::pointwise_supported(q.Cin, q.Cout) &&
+                   !(forced && *forced);
 
     *out = p;
     *workspace_bytes = p->ws_bytes;
@@ -258,13 +261,27 @@ conv3d_status conv3d_plan_query(conv3d_plan_t p, conv3d_plan_info *info) {
     info->gemm_n = p->prm.Cout;
     info->gemm_k = p->prm.K;
     info->flops = p->flops;
+    info->workspace_bytes = p->ws_bytes;
+    if (p->streaming) {
+        const int bm = c3d::kPointwiseRowsPerTile(p->prm.Cin);
+        const int64_t ntiles = (p->prm.M + bm - 1) / bm;
+        info->tile_m = bm;
+        info->tile_n = 128;
+        info->tile_k = p->prm.Cin;
+        info->stages = 2;
+        info->threads = 256;
+        const int lds = 2 * bm * p->prm.Cin * 2 + 4 * bm * 64;
+        const int per_cu = (160 * 1024 / lds) < 4 ? (160 * 1024 / lds) : 4;
+        info->grid = (ntiles < 256 * per_cu ? ntiles : 256 * per_cu) * ((p->prm.Cout + 127) / 128);
+        snprintf(info->kernel_name, sizeof(info->kernel_name), "conv1x1_stream_cin%d", p->prm.Cin);
+        return ok();
+    }
     info->tile_m = p->tile->bm;
     info->tile_n = p->tile->bn;
     info->tile_k = p->tile->bk;
     info->stages = p->tile->stages;
     info->threads = p->tile->threads;
     info->grid = p->prm.tiles;
-    info->workspace_bytes = p->ws_bytes;
     snprintf(info->kernel_name, sizeof(info->kernel_name), "conv3d_igemm_%s%s", p->tile->name,
              p->tail ? "_tail" : "");
     return ok();
@@ -310,6 +327,20 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
         hipError_t e = c3d::launch_fold_taps(q.w, w2, p->d.c_out, p->d.kt, p->fold_khwc, p->fold_lo, p->fold_hi, s);
         if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "fold launch: %s", hipGetErrorString(e));
         q.w = w2;
+    }
+    if (p->streaming) {
+        c3d::PwParams pw;
+        pw.x = q.x;
+        pw.w = q.w;
+        pw.bias = q.bias;
+        pw.res = q.res;
+        pw.y = q.y;
+        pw.Cin = q.Cin;
+        pw.Cout = q.Cout;
+        pw.M = q.M;
+        hipError_t e = c3d::launch_pointwise(pw, s);
+        if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "pointwise launch: %s", hipGetErrorString(e));
+        return ok();
     }
     hipError_t e = (p->tail ? p->tile->launch_tail : p->tile->launch_full)(q, s);
     if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "conv launch: %s", hipGetErrorString(e));

@@ -47,6 +47,20 @@ struct TileCfg {
 
 const TileCfg *tile_table(int *count);
 
+// 1x1x1 convolution without padding: a streaming GEMM over voxels.
+struct PwParams {
+    const _Float16 *x;     // [M][Cin]
+    const _Float16 *w;     // [Cout][Cin]
+    const _Float16 *bias;  // [Cout] or null
+    const _Float16 *res;   // [M][Cout] or null
+    _Float16 *y;           // [M][Cout]
+    int32_t Cin, Cout;
+    int64_t M;
+};
+bool pointwise_supported(int32_t cin, int32_t cout);
+hipError_t launch_pointwise(const PwParams &p, hipStream_t s);
+constexpr int kPointwiseRowsPerTile(int) { return 64; }
+
 // Sum of the temporal taps tau in [tau_lo, tau_hi] of w [Cout][kt][khw*Cin]
 // into w2 [Cout][khw*Cin], in fp32, rounded once to fp16.
 hipError_t launch_fold_taps(const _Float16 *w, _Float16 *w2, int32_t cout, int32_t kt,

@@ -137,16 +137,37 @@ __global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(const _Float16 *_
     w.n = cnt;
     w.mean = cnt > 0.0f ? K + s1 / cnt : 0.0f;
     w.m2 = cnt > 0.0f ? fmaxf(s2 - s1 * (s1 / cnt), 0.0f) : 0.0f;
+    // Lanes l and l ^ off (off a multiple of a power-of-two vpv) hold the same
+    // channel vector: merge them with shuffles first, so that only one entry
+    // per (wave, vector) goes through LDS.
+    const bool shuffled = vpv <= 64 && (vpv & (vpv - 1)) == 0 && nthr % 64 == 0;
+    if (shuffled) {
+        for (int off = vpv; off < 64; off <<= 1) {
+            Welford o;
+            o.n = __shfl_xor(w.n, off);
+            o.mean = __shfl_xor(w.mean, off);
+            o.m2 = __shfl_xor(w.m2, off);
+            w = chan_merge(w, o);
+        }
+    }
     red[tid] = make_float4(w.n, w.mean, w.m2, 0.0f);
     __syncthreads();
 
-    // merge the threads of each group: threads t with (t % vpv) / vpg == g
+    // merge the entries of each group (its vpg channel vectors, over all voxels)
     for (int g = tid; g < groups; g += nthr) {
         Welford acc = {0.0f, 0.0f, 0.0f};
-        for (int t = 0; t < nthr; ++t) {
-            if ((t % vpv) / vpg != g) continue;
-            const float4 e = red[t];
-            acc = chan_merge(acc, Welford{e.x, e.y, e.z});
+        if (shuffled) {
+            for (int wave = 0; wave < nthr / 64; ++wave)
+                for (int v = g * vpg; v < (g + 1) * vpg; ++v) {
+                    const float4 e = red[wave * 64 + v];
+                    acc = chan_merge(acc, Welford{e.x, e.y, e.z});
+                }
+        } else {
+            for (int t = 0; t < nthr; ++t) {
+                if ((t % vpv) / vpg != g) continue;
+                const float4 e = red[t];
+                acc = chan_merge(acc, Welford{e.x, e.y, e.z});
+            }
         }
         part[((size_t)n * sb + b) * groups + g] = make_float4(acc.n, acc.mean, acc.m2, 0.0f);
     }

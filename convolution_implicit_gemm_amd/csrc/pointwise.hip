@@ -1,0 +1,235 @@
+// 1x1x1 convolution (a plain GEMM over voxels) as an HBM-bound stream on gfx950.
+//
+// y[m][co] = bias[co] (+ res[m][co]) + sum_ci x[m][ci] * w[co][ci] with no
+// padding: every output voxel reads exactly its own input row.  At 256 -> 128
+// channels the arithmetic intensity is ~85 flop/byte, far below the MI355X
+// ridge, so the kernel is designed around moving bytes:
+//  * persistent blocks (two or more per CU), each streaming 64-row tiles of
+//    input through a double-buffered, bank-swizzled LDS ring with
+//    buffer_load ... lds (no VGPR staging);
+//  * each wave keeps its 32 output channels x all Cin of weights in VGPRs as
+//    MFMA A-fragments, loaded once per block;
+//  * every tile gets its own buffer resource spanning exactly its valid rows,
+//    so rows past M read as zeros through the range check;
+//  * fp16 MFMA 32x32x16 with fp32 accumulation; bias / residual added in fp32,
+//    one RNE rounding; the rounded tile is staged in LDS so that every store
+//    is a 16-byte piece of a whole output row.
+// Each K-iteration ends with s_waitcnt vmcnt(0): loads and stores share one
+// counter on gfx9, so the kernel never relies on their relative completion
+// order; the second block per CU keeps memory busy meanwhile.
+#include "c3d_internal.h"
+
+namespace c3d {
+
+typedef _Float16 pw_half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 pw_half4 __attribute__((ext_vector_type(4)));
+typedef float pw_f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void pw_lds_void;
+
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t pw_rsrc;
+#else
+struct pw_rsrc {
+    uint32_t w[4];
+};
+#endif
+
+namespace {
+
+__device__ __forceinline__ pw_rsrc pw_make_rsrc(const void *base, uint32_t bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+#else
+    (void)base;
+    (void)bytes;
+    return pw_rsrc{};
+#endif
+}
+
+__device__ __forceinline__ void pw_dma16(pw_rsrc r, char *lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (pw_lds_void *)lds, 16, voff, 0, 0, 0);
+#else
+    (void)r;
+    (void)lds;
+    (void)voff;
+#endif
+}
+
+__device__ __forceinline__ void pw_wait_all_and_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// 16-byte chunk swizzle within a row of CPR chunks: 32 consecutive rows read at
+// one logical chunk land on distinct banks in every 8- and 16-lane group.
+template <int CPR>
+__device__ __forceinline__ int pw_swz(int row) {
+    if constexpr (CPR >= 16)
+        return row & 15;
+    else
+        return (row ^ ((row >> 3) & 1)) & 7;
+}
+
+constexpr int kPwRows = 64;   // voxels per tile
+constexpr int kPwWaves = 4;   // 4 x 32 output channels per block
+
+template <int CIN>
+__global__ __launch_bounds__(256, 2) void pointwise_kernel(PwParams p) {
+    constexpr int RB = CIN * 2;                 // bytes per input row
+    constexpr int CPR = CIN / 8;                // 16-byte chunks per row
+    constexpr int BM = kPwRows;                 // rows per tile
+    constexpr int TILE_BYTES = BM * RB;
+    constexpr int RPI = 1024 / RB;              // rows per 1 KiB load instruction
+    constexpr int NI = TILE_BYTES / 1024 / kPwWaves;  // load instructions per wave per tile
+    constexpr int KF = CIN / 16;                // MFMA k-steps
+    constexpr int SUB = BM / 32;                // 32-voxel sub-tiles per tile
+    static_assert(RB <= 1024 && 1024 % RB == 0 && NI >= 1, "CIN in {64, 128, 256, 512}");
+
+    __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char obuf[kPwWaves * BM * 64];  // output staging
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int co0 = blockIdx.y * (32 * kPwWaves) + wv * 32;
+    const bool live = co0 < p.Cout;  // wave-uniform
+    const int rrow = lane & 31, rhi = lane >> 5;
+
+    // weights of this wave's 32 output channels, as A-fragments for every k-step
+    pw_half8 wf[KF];
+#pragma unroll
+    for (int f = 0; f < KF; ++f) {
+        if (live)
+            wf[f] = *reinterpret_cast<const pw_half8 *>(p.w + (int64_t)(co0 + rrow) * CIN + 16 * f + 8 * rhi);
+        else
+            wf[f] = pw_half8{};
+    }
+
+    // per-lane tile-relative source offsets of this wave's load instructions
+    uint32_t voff[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int q = j * kPwWaves + wv;
+        const int row = q * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ pw_swz<CPR>(row);
+        voff[j] = (uint32_t)(row * RB + c * 16);
+    }
+    int koff[KF];
+#pragma unroll
+    for (int f = 0; f < KF; ++f) koff[f] = rrow * RB + (((2 * f + rhi) ^ pw_swz<CPR>(rrow)) * 16);
+
+    const int M = (int)p.M;
+    const int ntiles = (M + BM - 1) / BM;
+    auto issue = [&](int tile, int buf) {
+        const int m0 = tile * BM;
+        const int rows = M - m0 < BM ? M - m0 : BM;
+        const pw_rsrc r = pw_make_rsrc(p.x + (int64_t)m0 * CIN, (uint32_t)(rows * RB));
+        char *sb = smem + buf * TILE_BYTES;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) pw_dma16(r, sb + (j * kPwWaves + wv) * 1024, voff[j]);
+    };
+
+    int tile = blockIdx.x;
+    if (tile < ntiles) issue(tile, 0);
+    for (int it = 0; tile < ntiles; ++it, tile += gridDim.x) {
+        pw_wait_all_and_barrier();  // this tile landed; everyone is done with the other buffer
+        const int next = tile + (int)gridDim.x;
+        if (next < ntiles) issue(next, (it + 1) & 1);
+        if (!live) continue;
+        const char *sb = smem + (it & 1) * TILE_BYTES;
+        pw_f32x16 acc[SUB];
+#pragma unroll
+        for (int s = 0; s < SUB; ++s)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[s][e] = 0.0f;
+#pragma unroll
+        for (int f = 0; f < KF; ++f) {
+#pragma unroll
+            for (int s = 0; s < SUB; ++s) {
+                const pw_half8 b = *reinterpret_cast<const pw_half8 *>(sb + s * 32 * RB + koff[f]);
+                acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[f], b, acc[s], 0, 0, 0);
+            }
+        }
+        // epilogue: + bias (+ residual) in fp32 and one RNE rounding in registers,
+        // then through LDS so that the block writes whole output rows with
+        // 16-byte stores (scattered 8-byte stores of 256-byte rows waste most of
+        // each memory transaction).  Lane holds channels co0 + 8g + 4*(lane/32) + e
+        // of voxel lane%32.
+        const int m0 = tile * BM;
+        char *ob = obuf + wv * (BM * 64);  // this wave's [BM voxels][32 ch] fp16, row-swizzled
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int co = co0 + 8 * g + 4 * rhi;
+            float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.bias) {
+                const pw_half4 b4 = *reinterpret_cast<const pw_half4 *>(p.bias + co);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[e] = (float)b4[e];
+            }
+#pragma unroll
+            for (int s = 0; s < SUB; ++s) {
+                const int vrow = s * 32 + rrow;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[s][4 * g + e] + bv[e];
+                if (p.res && m0 + vrow < M) {
+                    const pw_half4 r4 = *reinterpret_cast<const pw_half4 *>(p.res + (int64_t)(m0 + vrow) * p.Cout + co);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] += (float)r4[e];
+                }
+                pw_half4 h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[e];
+                // 8-byte unit (2g + rhi) of the 64-byte row, xor-swizzled by the row
+                *reinterpret_cast<pw_half4 *>(ob + vrow * 64 + (((2 * g + rhi) ^ (vrow & 7)) * 8)) = h;
+            }
+        }
+        // each lane stores 16 bytes; 4 lanes cover this wave's 64-byte slice of a row
+#pragma unroll
+        for (int q = 0; q < BM / 16; ++q) {
+            const int vrow = q * 16 + (lane >> 2), part = lane & 3;
+            const int m = m0 + vrow;
+            const int u0 = (2 * part) ^ (vrow & 7), u1 = (2 * part + 1) ^ (vrow & 7);
+            const pw_half4 lo = *reinterpret_cast<const pw_half4 *>(ob + vrow * 64 + u0 * 8);
+            const pw_half4 hi = *reinterpret_cast<const pw_half4 *>(ob + vrow * 64 + u1 * 8);
+            if (m < M) {
+                pw_half8 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = lo[e];
+                    v[4 + e] = hi[e];
+                }
+                *reinterpret_cast<pw_half8 *>(p.y + (int64_t)m * p.Cout + co0 + part * 8) = v;
+            }
+        }
+    }
+    pw_wait_all_and_barrier();
+}
+
+template <int CIN>
+hipError_t launch_pw(const PwParams &p, hipStream_t s) {
+    // as many resident blocks as LDS allows, up to four per CU
+    constexpr int lds = 2 * kPwRows * CIN * 2 + kPwWaves * kPwRows * 64;
+    constexpr int per_cu = (160 * 1024 / lds) < 4 ? (160 * 1024 / lds) : 4;
+    const int64_t ntiles = (p.M + kPwRows - 1) / kPwRows;
+    const int64_t cap = 256 * per_cu;
+    const int64_t blocks = ntiles < cap ? ntiles : cap;
+    const unsigned gy = (unsigned)((p.Cout + 32 * kPwWaves - 1) / (32 * kPwWaves));
+    hipLaunchKernelGGL(pointwise_kernel<CIN>, dim3((unsigned)blocks, gy), dim3(64 * kPwWaves), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool pointwise_supported(int32_t cin, int32_t cout) {
+    return (cin == 64 || cin == 128 || cin == 256 || cin == 512) && cout % 32 == 0;
+}
+
+hipError_t launch_pointwise(const PwParams &p, hipStream_t s) {
+    switch (p.Cin) {
+        case 64: return launch_pw<64>(p, s);
+        case 128: return launch_pw<128>(p, s);
+        case 256: return launch_pw<256>(p, s);
+        case 512: return launch_pw<512>(p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace c3d

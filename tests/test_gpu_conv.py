@@ -209,3 +209,34 @@ def test_channel_changing_stage_full_size_sampled():
     assert info.path == c3d.CONV3D_PATH_POINTWISE
     d2 = {"x": y1h, "w": d["w2"], "b": d["b2"]}
     check_sampled(s2, d2, y2, count=20000, seed=15)
+
+
+PW_CASES = [(64, 32), (128, 160), (256, 128), (512, 96), (256, 256)]
+
+
+@pytest.mark.parametrize("cin,cout", PW_CASES)
+def test_streaming_pointwise_exact(cin, cout):
+    s = ConvShape(2, 3, 5, 7, cin, cout, kt=1, kh=1, kw=1, pad_t_front=0, pad_t_back=0, pad_h=0,
+                  pad_w=0, tmode=Z)  # M = 210 voxels: a ragged last tile
+    x = ternary(s.x_shape, 60 + cin)
+    w = ternary(s.w_shape, 61 + cout)
+    b = np.random.default_rng(62).integers(-2, 3, s.cout).astype(np.float16)
+    y, info = run_conv(s, x, w, b)
+    assert info.kernel_name.decode() == "conv1x1_stream_cin%d" % cin
+    ref, _ = oracle_full(s, x, w, b)
+    assert np.array_equal(y.astype(np.float64), ref)
+    # the general implicit-GEMM kernel, forced by naming a tile, gives the same bits here
+    yg, info_g = run_conv(s, x, w, b, tile="m256n128k64s2w4")
+    assert info_g.kernel_name.decode().startswith("conv3d_igemm_")
+    assert np.array_equal(yg, y)
+
+
+def test_streaming_pointwise_bias_residual_bound():
+    s = ConvShape(1, 4, 9, 11, 256, 128, kt=1, kh=1, kw=1, pad_t_front=0, pad_t_back=0, pad_h=0,
+                  pad_w=0, tmode=Z)
+    d = workloads.conv_inputs(s, 640)
+    res = workloads.normal_f16(np.random.SeedSequence(641), out_dims(s))
+    y, info = run_conv(s, d["x"], d["w"], d["b"], res=res)
+    assert info.kernel_name.decode().startswith("conv1x1_stream")
+    ref, mag = oracle_full(s, d["x"], d["w"], d["b"], res)
+    assert_conv_close(y, ref, mag, "pointwise + residual")
