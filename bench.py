@@ -75,6 +75,12 @@ def time_steps(fn, steps, warmup, torch):
     return wall * 1e3 / steps, per
 
 
+def ws_for(plan, torch, dev):
+    if not plan.workspace_bytes:
+        return None
+    return torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+
+
 def desc_of(c3d, s, flags):
     return c3d.make_desc(s.n, s.t, s.h, s.w, s.cin, s.cout, s.kt, s.kh, s.kw, s.pad_t_front,
                          s.pad_t_back, s.pad_h, s.pad_w, s.tmode, flags)
@@ -155,9 +161,10 @@ def main():
     info = plan.info()
     x, w, b = T(d1["x"]), T(d1["w"]), T(d1["b"])
     y = torch.empty(out_dims(s1), dtype=torch.float16, device=dev)
+    ws = ws_for(plan, torch, dev)
 
     def step():
-        c3d.conv3d_forward(plan, x, w, b, None, y)
+        c3d.conv3d_forward(plan, x, w, b, None, y, ws)
 
     log("timing %d steps after %d warmup" % (args.steps, args.warmup))
     ms, per = time_steps(step, args.steps, args.warmup, torch)
@@ -197,6 +204,7 @@ def main():
     thw = s4.t * s4.h * s4.w
     bp1 = c3d.conv3d_plan(desc_of(c3d, s4, c3d.CONV3D_F_BIAS))
     bp2 = c3d.conv3d_plan(desc_of(c3d, s4, c3d.CONV3D_F_BIAS | c3d.CONV3D_F_RESIDUAL))
+    bws1, bws2 = ws_for(bp1, torch, dev), ws_for(bp2, torch, dev)
     gws = torch.zeros(c3d.groupnorm_silu_workspace(1, thw, s4.cin, 32), dtype=torch.uint8,
                       device=dev)
     bx = T(d4["x"])
@@ -205,9 +213,9 @@ def main():
 
     def block():
         c3d.groupnorm_silu(bx, bt["gamma1"], bt["beta1"], a1, 1, thw, s4.cin, 32, 1e-6, True, gws)
-        c3d.conv3d_forward(bp1, a1, bt["w1"], bt["b1"], None, c1)
+        c3d.conv3d_forward(bp1, a1, bt["w1"], bt["b1"], None, c1, bws1)
         c3d.groupnorm_silu(c1, bt["gamma2"], bt["beta2"], a2, 1, thw, s4.cout, 32, 1e-6, True, gws)
-        c3d.conv3d_forward(bp2, a2, bt["w2"], bt["b2"], bx, out)
+        c3d.conv3d_forward(bp2, a2, bt["w2"], bt["b2"], bx, out, bws2)
 
     bms, bper = time_steps(block, max(5, args.steps // 2), max(2, args.warmup), torch)
     result["decoder_block_ms"] = round(sum(bper) / len(bper), 4)
@@ -219,7 +227,7 @@ def main():
         conv_flops = bp1.info().flops
 
         def conv_only():
-            c3d.conv3d_forward(bp1, a1, bt["w1"], bt["b1"], None, c1)
+            c3d.conv3d_forward(bp1, a1, bt["w1"], bt["b1"], None, c1, bws1)
         _, p = time_steps(conv_only, 10, 2, torch)
         t = sum(p) / len(p)
         kern["causal_conv_256_T17"] = {"ms": round(t, 4), "TFLOP/s": round(conv_flops / t / 1e9, 1),
@@ -237,7 +245,7 @@ def main():
 
         s1f = workloads.CAUSAL_256_T1
         pt1 = c3d.conv3d_plan(desc_of(c3d, s1f, c3d.CONV3D_F_BIAS))
-        ws1 = torch.empty(pt1.workspace_bytes, dtype=torch.uint8, device=dev)
+        ws1 = ws_for(pt1, torch, dev)
         x1 = bx[:, :1].contiguous()
         y1 = torch.empty(out_dims(s1f), dtype=torch.float16, device=dev)
 
@@ -256,13 +264,14 @@ def main():
         p3 = c3d.conv3d_plan(desc_of(c3d, s3, c3d.CONV3D_F_BIAS))
         p3b = c3d.conv3d_plan(desc_of(c3d, s3b, c3d.CONV3D_F_BIAS))
         x3, w3, b3 = T(d3["x"]), T(d3["w"]), T(d3["b"])
+        ws3 = ws_for(p3, torch, dev)
         del d3["x"]
         y3 = torch.empty(out_dims(s3), dtype=torch.float16, device=dev)
         w3b, b3b = T(d3["w2"]), T(d3["b2"])
         y3b = torch.empty(out_dims(s3b), dtype=torch.float16, device=dev)
 
         def st1():
-            c3d.conv3d_forward(p3, x3, w3, b3, None, y3)
+            c3d.conv3d_forward(p3, x3, w3, b3, None, y3, ws3)
         _, p = time_steps(st1, 3, 1, torch)
         t = sum(p) / len(p)
         kern["causal_conv_512to256_T33_256x256"] = {"ms": round(t, 3),

@@ -51,7 +51,8 @@ class conv3d_plan_info(ctypes.Structure):
                 ("gemm_k", ctypes.c_int64), ("flops", ctypes.c_double), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32), ("stages", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("grid", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_size_t), ("kernel_name", ctypes.c_char * 64)]
+                ("workspace_bytes", ctypes.c_size_t), ("kernel_name", ctypes.c_char * 64),
+                ("split_tiles", ctypes.c_int32), ("split_pieces", ctypes.c_int32)]
 
 
 class Conv3dError(RuntimeError):

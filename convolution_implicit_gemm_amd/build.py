@@ -47,10 +47,12 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)
     nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
-    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
+    # a kernel instantiation the host pass dropped leaves its launch stub
+    # undefined; any other undefined symbol of our namespace is a build error too
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "3c3d" in ln]
     if missing:
         os.remove(tmp)
-        raise RuntimeError("kernel launch stubs missing from the host objects: %s" % missing[:3])
+        raise RuntimeError("undefined library symbols (e.g. dropped kernel launch stubs): %s" % missing[:3])
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

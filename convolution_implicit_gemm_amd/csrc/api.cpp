@@ -72,15 +72,42 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Relative cost of a tile shape per unit of MFMA work: bigger tiles reuse
-// each LDS byte more often.  Used only to rank candidates.
-double tile_efficiency(const c3d::TileCfg &t) {
-    const double area = (double)t.bm * t.bn;
-    if (area >= 65536) return 1.0;
-    if (area >= 32768) return 0.9;
-    if (area >= 16384) return 0.8;
-    if (area >= 8192) return 0.6;
-    return 0.45;
+// How one tile configuration would run a conv: `dp` whole tiles, then
+// `sk` tiles split into `pieces` K-pieces plus a fixup pass.
+struct Decomp {
+    int64_t dp, sk;
+    int pieces;
+    double seconds;
+};
+
+constexpr double kBestRatePerCU = 1130e12 / kCUs;  // flop/s of the best tile config, per CU
+constexpr double kFixupBytesPerSec = 4.5e12;
+constexpr double kLaunchSeconds = 4e-6;
+constexpr size_t kMaxSplitWorkspace = (size_t)256 << 20;
+
+// Cost model: each CU runs ceil(tiles/CUs) whole tiles at the configuration's
+// measured rate; a split run fills the last wave with K-pieces instead and
+// pays for writing and summing fp32 partial tiles.  mode: -1 never split,
+// 0 model decides, 1 split whenever tiles do not fill whole waves.
+Decomp decompose(const c3d::TileCfg &t, int64_t tiles, int niter, int mode) {
+    const double f_iter = 2.0 * t.bm * t.bn * t.bk;
+    const double t_iter = f_iter / (kBestRatePerCU * t.rate);
+    Decomp best = {tiles, 0, 1, (double)((tiles + kCUs - 1) / kCUs) * niter * t_iter};
+    const int occ = (int)(kLdsPerCU / t.lds_bytes);
+    const int64_t full = tiles / kCUs, rem = tiles % kCUs;
+    if (mode < 0 || occ != 1 || rem == 0) return best;
+    Decomp split = {0, 0, 0, 0.0};
+    for (int pieces = 2; pieces <= 16 && pieces * 4 <= niter; ++pieces) {
+        const size_t ws = (size_t)rem * pieces * t.bm * t.bn * 4;
+        if (ws > kMaxSplitWorkspace) break;
+        const int64_t waves2 = (rem * pieces + kCUs - 1) / kCUs;
+        const double sec = ((double)full * niter + (double)waves2 * ((niter + pieces - 1) / pieces)) * t_iter +
+                           (double)ws * 2 / kFixupBytesPerSec + kLaunchSeconds;
+        if (!split.pieces || sec < split.seconds) split = {full * kCUs, rem, pieces, sec};
+    }
+    // split only for a clear win (or when forced)
+    if (split.pieces && (mode > 0 || split.seconds < best.seconds * 0.95)) return split;
+    return best;
 }
 
 }  // namespace
@@ -94,6 +121,7 @@ struct conv3d_plan_s {
     bool tail;
     int fold_lo, fold_hi;
     int64_t fold_khwc;
+    size_t ws_fold;       // bytes of folded weights at the start of the workspace
     size_t ws_bytes;
     int64_t x_elems, w_elems, y_elems;
     double flops;
@@ -167,7 +195,7 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
             p->fold_lo = p->fold_hi = d->pad_t_front;  // the only tap inside [0, 1)
         }
         p->fold_khwc = (int64_t)d->kh * d->kw * d->c_in;
-        p->ws_bytes = ((size_t)d->c_out * p->fold_khwc * 2 + 255) & ~(size_t)255;
+        p->ws_fold = ((size_t)d->c_out * p->fold_khwc * 2 + 255) & ~(size_t)255;
     } else if (d->kt == 1 && d->kh == 1 && d->kw == 1) {
         path = CONV3D_PATH_POINTWISE;
     }
@@ -192,31 +220,24 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
     q.K = q.kt * q.kh * q.kw * q.Cin;
     q.M = out_vox;
 
-    // tile choice: forced by CONV3D_TILE, else the cheapest by a wave model
+    // tile and decomposition: CONV3D_TILE forces the configuration,
+    // CONV3D_STREAMK=0/1 forbids/forces splitting; otherwise the cost model picks
     int ntile = 0;
     const c3d::TileCfg *tiles = c3d::tile_table(&ntile);
     const char *forced = getenv("CONV3D_TILE");
+    const char *skenv = getenv("CONV3D_STREAMK");
+    const int skmode = skenv && *skenv == '0' ? -1 : (skenv && *skenv == '1' ? 1 : 0);
     const c3d::TileCfg *best = nullptr;
-    double best_cost = 0.0;
+    Decomp best_d = {0, 0, 1, 0.0};
     for (int i = 0; i < ntile; ++i) {
         const c3d::TileCfg &t = tiles[i];
-        if (forced && *forced) {
-            if (strcmp(forced, t.name) == 0) best = &t;
-            continue;
-        }
+        if (forced && *forced && strcmp(forced, t.name) != 0) continue;
         const int64_t mt = (q.M + t.bm - 1) / t.bm, nt = (q.Cout + t.bn - 1) / t.bn;
-        const int64_t ntiles = mt * nt;
-        int occ = (int)(kLdsPerCU / t.lds_bytes);
-        if (occ > 2048 / t.threads) occ = 2048 / t.threads;
-        if (occ < 1) occ = 1;
-        const int64_t slots = (int64_t)kCUs * occ;
-        const int64_t waves = (ntiles + slots - 1) / slots;
         const int cpt = (q.Cin + t.bk - 1) / t.bk;
-        const double kwork = (double)q.kt * q.kh * q.kw * cpt * t.bk;
-        const double cost = (double)waves * occ * t.bm * t.bn * kwork / tile_efficiency(t);
-        if (!best || cost < best_cost) {
+        const Decomp dcmp = decompose(t, mt * nt, q.kt * q.kh * q.kw * cpt, skmode);
+        if (!best || dcmp.seconds < best_d.seconds) {
             best = &t;
-            best_cost = cost;
+            best_d = dcmp;
         }
     }
     if (!best) {
@@ -241,9 +262,19 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
     q.m_tiles = (int)((q.M + best->bm - 1) / best->bm);
     q.n_tiles = (q.Cout + best->bn - 1) / best->bn;
     q.tiles = (int64_t)q.m_tiles * q.n_tiles;
+    q.dp_tiles = (int32_t)best_d.dp;
+    q.sk_tiles = (int32_t)best_d.sk;
+    q.sk_pieces = best_d.pieces;
+    q.partial = nullptr;
+    p->ws_bytes = p->ws_fold + (size_t)q.sk_tiles * q.sk_pieces * best->bm * best->bn * 4;
     p->flops = 2.0 * (double)q.M * q.Cout * q.K;
     p->streaming = path == CONV3D_PATH_POINTWISE && c3d::pointwise_supported(q.Cin, q.Cout) &&
                    !(forced && *forced);
+    if (p->streaming) {  // the streaming kernel neither splits K nor needs a workspace
+        q.dp_tiles = (int32_t)q.tiles;
+        q.sk_tiles = 0;
+        p->ws_bytes = p->ws_fold;
+    }
 
     *out = p;
     *workspace_bytes = p->ws_bytes;
@@ -281,7 +312,9 @@ conv3d_status conv3d_plan_query(conv3d_plan_t p, conv3d_plan_info *info) {
     info->tile_k = p->tile->bk;
     info->stages = p->tile->stages;
     info->threads = p->tile->threads;
-    info->grid = p->prm.tiles;
+    info->grid = p->prm.dp_tiles + (int64_t)p->prm.sk_tiles * p->prm.sk_pieces;
+    info->split_tiles = p->prm.sk_tiles;
+    info->split_pieces = p->prm.sk_tiles ? p->prm.sk_pieces : 0;
     snprintf(info->kernel_name, sizeof(info->kernel_name), "conv3d_igemm_%s%s", p->tile->name,
              p->tail ? "_tail" : "");
     return ok();
@@ -309,7 +342,8 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
             return fail(CONV3D_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p->ws_bytes,
                         workspace ? workspace_bytes : (size_t)0);
         if (overlap(workspace, p->ws_bytes, y, yb) || overlap(workspace, p->ws_bytes, x, (size_t)p->x_elems * 2) ||
-            overlap(workspace, p->ws_bytes, weight, (size_t)p->w_elems * 2))
+            overlap(workspace, p->ws_bytes, weight, (size_t)p->w_elems * 2) ||
+            (has_res && overlap(workspace, p->ws_bytes, residual, yb)))
             return fail(CONV3D_ERR_INVALID_ARG, "workspace overlaps a tensor");
     }
     conv3d_status st = check_device();
@@ -322,6 +356,7 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
     q.bias = has_bias ? static_cast<const _Float16 *>(bias) : nullptr;
     q.res = has_res ? static_cast<const _Float16 *>(residual) : nullptr;
     q.y = static_cast<_Float16 *>(y);
+    if (q.sk_tiles) q.partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + p->ws_fold);
     if (p->path == CONV3D_PATH_T1_FOLD) {
         _Float16 *w2 = static_cast<_Float16 *>(workspace);
         hipError_t e = c3d::launch_fold_taps(q.w, w2, p->d.c_out, p->d.kt, p->fold_khwc, p->fold_lo, p->fold_hi, s);
@@ -344,6 +379,10 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
     }
     hipError_t e = (p->tail ? p->tile->launch_tail : p->tile->launch_full)(q, s);
     if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "conv launch: %s", hipGetErrorString(e));
+    if (q.sk_tiles) {
+        e = p->tile->launch_fixup(q, s);
+        if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "fixup launch: %s", hipGetErrorString(e));
+    }
     return ok();
 }
 

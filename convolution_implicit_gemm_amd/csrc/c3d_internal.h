@@ -24,6 +24,10 @@ struct ConvParams {
     int32_t cpt;           // K-iterations per tap: ceil(Cin / BK)
     int32_t niter;         // kt*kh*kw*cpt
     int32_t m_tiles, n_tiles;
+    int32_t dp_tiles;      // tiles [0, dp_tiles) run whole, one workgroup each
+    int32_t sk_tiles;      // tiles [dp_tiles, dp_tiles+sk_tiles) run as sk_pieces K-pieces
+    int32_t sk_pieces;
+    float *partial;        // [sk_tiles*sk_pieces][BM*BN] fp32 partial tiles (workspace)
     int32_t in_vox;        // N*T*H*W input voxels
     uint32_t w_bytes;      // Cout*K*2, below 2^30
     int64_t M;             // N*To*Ho*Wo, below 2^30
@@ -41,8 +45,10 @@ struct TileCfg {
     const char *name;
     int bm, bn, bk, stages, threads;
     size_t lds_bytes;
+    double rate;               // measured relative throughput per CU (1 = best)
     ConvLaunchFn launch_full;  // Cin % bk == 0
     ConvLaunchFn launch_tail;  // any Cin % 8 == 0 (channel tail zero-filled per tap)
+    ConvLaunchFn launch_fixup; // sums the K-pieces of the split tiles, then the epilogue
 };
 
 const TileCfg *tile_table(int *count);

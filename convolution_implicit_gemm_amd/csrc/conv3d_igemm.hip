@@ -112,6 +112,47 @@ __device__ __forceinline__ void dma16(buf_rsrc r, char *lds, uint32_t voff, uint
 // Offset that is always past a buffer's record count (records stay below 2^30).
 constexpr uint32_t kOOB = 0x80000000u;
 
+// Epilogue of one tile: + bias (+ residual) in fp32, one RNE rounding, NDHWC
+// store.  Lane holds, for sub-tile (i, j) and register 4g+e: channel
+// co = 8g + 4*(lane/32) + e of the sub-tile, voxel m = lane % 32.
+template <int TN, int TM, int WN, int WM>
+__device__ __forceinline__ void store_tile(const ConvParams &p, const f32x16 (&acc)[TN][TM], int m0, int n0, int wmi,
+                                           int wni, int rrow, int rhi) {
+    const int M = (int)p.M;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int co = n0 + wni * WN + i * 32 + 8 * g + 4 * rhi;
+            if (co >= p.Cout) continue;
+            f32x4 bv = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.bias) {
+                const half4_t b4 = *reinterpret_cast<const half4_t *>(p.bias + co);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[e] = (float)b4[e];
+            }
+#pragma unroll
+            for (int j = 0; j < TM; ++j) {
+                const int m = m0 + wmi * WM + j * 32 + rrow;
+                if (m >= M) continue;
+                const int64_t o = (int64_t)m * p.Cout + co;
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] + bv[e];
+                if (p.res) {
+                    const half4_t r4 = *reinterpret_cast<const half4_t *>(p.res + o);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] += (float)r4[e];
+                }
+                half4_t h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[e];
+                *reinterpret_cast<half4_t *>(p.y + o) = h;
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool TAIL>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kernel(ConvParams p) {
     constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN;
@@ -133,12 +174,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // XCD-aware renumbering: XCD x = blockIdx mod 8 gets a contiguous tile range.
-    const int nblk = (int)p.tiles;
+    // Work: workgroups [0, dp_tiles) each run one whole tile, renumbered so that
+    // XCD x (= workgroup id mod 8) walks a contiguous tile range; the rest each
+    // run one K-piece [it0, it1) of a split tile and leave an fp32 partial.
     const int bid = blockIdx.x;
-    const int per = nblk >> 3, rem = nblk & 7;
-    const int xcd = bid & 7;
-    const int tile = xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3);
+    int tile, it0 = 0, it1 = p.niter, slot = -1;
+    if (bid < p.dp_tiles) {
+        const int per = p.dp_tiles >> 3, rem = p.dp_tiles & 7;
+        const int xcd = bid & 7;
+        tile = xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3);
+    } else {
+        slot = bid - p.dp_tiles;
+        const int piece = slot % p.sk_pieces;
+        tile = p.dp_tiles + slot / p.sk_pieces;
+        it0 = (int)((int64_t)p.niter * piece / p.sk_pieces);
+        it1 = (int)((int64_t)p.niter * (piece + 1) / p.sk_pieces);
+    }
     const int mt = tile / p.n_tiles, nt = tile - mt * p.n_tiles;
     const int m0 = mt * BM;
     const int n0 = nt * BN;
@@ -213,9 +264,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
     // scalar offset.  After the last stage the state freezes, so the extra
     // fetches that keep every wave's load count constant re-read valid data
     // into a buffer nobody reads again.
-    const int niter = p.niter;
     const int t_lo = p.replicate ? 0 : -(1 << 20), t_hi = p.replicate ? T - 1 : (1 << 20);
-    int ld_it = 0, ld_ci = 0, ld_tap = 0, ld_tau = 0, ld_r = 0, ld_s = 0;
+    int ld_it = it0, ld_ci = (it0 % p.cpt) * BK, ld_tap = it0 / p.cpt;
+    int ld_s = ld_tap % p.kw, ld_r = (ld_tap / p.kw) % p.kh, ld_tau = ld_tap / (p.kw * p.kh);
     uint32_t a_voff[LA];
     auto set_offsets = [&]() {
         const int dr = ld_r - p.ph, ds = ld_s - p.pw;
@@ -258,7 +309,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
             }
         }
         // advance (tau, r, s, ci0) with selects only; freeze after the last stage
-        const int step = ld_it + 1 < niter ? 1 : 0;
+        const int step = ld_it + 1 < it1 ? 1 : 0;
         ++ld_it;
         const int nci = ld_ci + BK * step;
         const int wrap = nci >= Cin ? 1 : 0;
@@ -323,8 +374,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
     wait_lds_and_loads<(STAGES - 1) * LOADS>();
     read_frags(smem, 0, 0);
 
-    for (int it = 0; it < niter; ++it) {
-        const int buf = it % STAGES;
+    for (int it = it0; it < it1; ++it) {
+        const int buf = (it - it0) % STAGES;
         const char *sb = smem + buf * STAGE_BYTES;
         // region A: k-steps 0..KS-2 of this stage; offsets of the next fetch
 #pragma unroll
@@ -349,68 +400,99 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
         // region B: refill this stage's buffer, read k-step 0 of the next stage,
         // and run the last k-step of this one meanwhile
         fire(buf);
-        read_frags(smem + ((it + 1) % STAGES) * STAGE_BYTES, 0, 0);
+        read_frags(smem + ((it - it0 + 1) % STAGES) * STAGE_BYTES, 0, 0);
         mfmas((KS - 1) & 1);
     }
     wait_lds_and_loads<0>();  // drain the extra fetches before LDS is released
 
-    // ---- epilogue: + bias (+ residual) in fp32, one RNE rounding, NDHWC store.
-    // Lane holds, for sub-tile (i, j) and register 4g+e: channel
-    // co = 8g + 4*(lane/32) + e of the sub-tile, voxel m = lane % 32.
+    if (slot >= 0) {
+        // a K-piece: leave the fp32 partial in fragment order, one float4 (4
+        // consecutive channels of one voxel) per lane per store: 1 KiB rows
+        f32x4 *pp = reinterpret_cast<f32x4 *>(p.partial + (size_t)slot * (BM * BN));
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
+        for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int co = n0 + wni * WN + i * 32 + 8 * g + 4 * rhi;
-            if (co >= p.Cout) continue;
-            f32x4 bv = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (p.bias) {
-                const half4_t b4 = *reinterpret_cast<const half4_t *>(p.bias + co);
+            for (int j = 0; j < TM; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) bv[e] = (float)b4[e];
-            }
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 v;
 #pragma unroll
-            for (int j = 0; j < TM; ++j) {
-                const int m = m0 + wmi * WM + j * 32 + rrow;
-                if (m >= M) continue;
-                const int64_t o = (int64_t)m * p.Cout + co;
-                f32x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] + bv[e];
-                if (p.res) {
-                    const half4_t r4 = *reinterpret_cast<const half4_t *>(p.res + o);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] += (float)r4[e];
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+                    pp[((((size_t)wv * TN + i) * TM + j) * 4 + g) * 64 + lane] = v;
                 }
-                half4_t h;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[e];
-                *reinterpret_cast<half4_t *>(p.y + o) = h;
-            }
-        }
+        return;
     }
+    store_tile<TN, TM, WN, WM>(p, acc, m0, n0, wmi, wni, rrow, rhi);
+}
+
+// Sums the K-pieces of the split tiles and applies the epilogue.  Flat over
+// float4 units of the fragment-order partials: unit u of tile t holds the 4
+// channels co = n0 + wni*WN + i*32 + 8g + 4*(lane/32) + e of voxel
+// m = m0 + wmi*WM + j*32 + lane%32, where u = (((wave*TN + i)*TM + j)*4 + g)*64 + lane.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(256) void conv3d_fixup_kernel(ConvParams p) {
+    constexpr int NWN = BN / WN, TM = WM / 32, TN = WN / 32, UNITS = BM * BN / 4;
+    const int64_t g_u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g_u >= (int64_t)p.sk_tiles * UNITS) return;
+    const int t = (int)(g_u / UNITS), u = (int)(g_u - (int64_t)t * UNITS);
+    const int lane = u & 63, g = (u >> 6) & 3;
+    const int j = (u >> 8) % TM, i = (u >> 8) / TM % TN, wave = (u >> 8) / (TM * TN);
+    const int tile = p.dp_tiles + t;
+    const int mt = tile / p.n_tiles, nt = tile - mt * p.n_tiles;
+    const int co = nt * BN + (wave % NWN) * WN + i * 32 + 8 * g + 4 * (lane >> 5);
+    const int m = mt * BM + (wave / NWN) * WM + j * 32 + (lane & 31);
+    const f32x4 *pp = reinterpret_cast<const f32x4 *>(p.partial) + (size_t)t * p.sk_pieces * UNITS + u;
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int piece = 0; piece < p.sk_pieces; ++piece) v += pp[(size_t)piece * UNITS];
+    if (co >= p.Cout || m >= (int)p.M) return;
+    if (p.bias) {
+        const half4_t b4 = *reinterpret_cast<const half4_t *>(p.bias + co);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += (float)b4[e];
+    }
+    const int64_t o = (int64_t)m * p.Cout + co;
+    if (p.res) {
+        const half4_t r4 = *reinterpret_cast<const half4_t *>(p.res + o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += (float)r4[e];
+    }
+    half4_t h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[e];
+    *reinterpret_cast<half4_t *>(p.y + o) = h;
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool TAIL>
 hipError_t launch_igemm(const ConvParams &p, hipStream_t s) {
     constexpr int threads = (BM / WM) * (BN / WN) * 64;
-    hipLaunchKernelGGL((conv3d_igemm_kernel<BM, BN, BK, WM, WN, STAGES, TAIL>), dim3((unsigned)p.tiles),
-                       dim3(threads), 0, s, p);
+    const unsigned grid = (unsigned)(p.dp_tiles + p.sk_tiles * p.sk_pieces);
+    hipLaunchKernelGGL((conv3d_igemm_kernel<BM, BN, BK, WM, WN, STAGES, TAIL>), dim3(grid), dim3(threads), 0, s, p);
     return hipGetLastError();
 }
 
-#define C3D_TILE(NAME, BM, BN, BK, WM, WN, ST)                                                  \
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_fixup(const ConvParams &p, hipStream_t s) {
+    const int64_t units = (int64_t)p.sk_tiles * (BM * BN / 4);
+    hipLaunchKernelGGL((conv3d_fixup_kernel<BM, BN, WM, WN>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s,
+                       p);
+    return hipGetLastError();
+}
+
+// rate: throughput per CU relative to the best configuration, measured on a
+// full-wave workload (causal 3x3x3, 512 -> 256, 256x256 frames)
+#define C3D_TILE(NAME, BM, BN, BK, WM, WN, ST, RATE)                                            \
     {NAME, BM, BN, BK, ST, (BM / WM) * (BN / WN) * 64, (size_t)(ST) * ((BM) + (BN)) * (BK) * 2, \
-     launch_igemm<BM, BN, BK, WM, WN, ST, false>, launch_igemm<BM, BN, BK, WM, WN, ST, true>}
+     RATE, launch_igemm<BM, BN, BK, WM, WN, ST, false>, launch_igemm<BM, BN, BK, WM, WN, ST, true>, \
+     launch_fixup<BM, BN, WM, WN>}
 
 static const TileCfg k_tiles[] = {
-    C3D_TILE("m256n256k64s2w4", 256, 256, 64, 128, 128, 2),
-    C3D_TILE("m256n256k32s4w4", 256, 256, 32, 128, 128, 4),
-    C3D_TILE("m256n256k64s2w8", 256, 256, 64, 64, 128, 2),
-    C3D_TILE("m256n128k64s2w4", 256, 128, 64, 128, 64, 2),
-    C3D_TILE("m128n128k64s3w4", 128, 128, 64, 64, 64, 3),
-    C3D_TILE("m128n64k64s2w4", 128, 64, 64, 32, 64, 2),
-    C3D_TILE("m128n32k32s2w4", 128, 32, 32, 32, 32, 2),
+    C3D_TILE("m256n256k64s2w4", 256, 256, 64, 128, 128, 2, 0.93),
+    C3D_TILE("m256n256k32s4w4", 256, 256, 32, 128, 128, 4, 0.89),
+    C3D_TILE("m256n256k64s2w8", 256, 256, 64, 64, 128, 2, 1.00),
+    C3D_TILE("m256n128k64s2w4", 256, 128, 64, 128, 64, 2, 0.83),
+    C3D_TILE("m128n128k64s3w4", 128, 128, 64, 64, 64, 3, 0.72),
+    C3D_TILE("m128n64k64s2w4", 128, 64, 64, 32, 64, 2, 0.68),
+    C3D_TILE("m128n32k32s2w4", 128, 32, 32, 32, 32, 2, 0.31),
 };
 
 int64_t tile_window_voxels(const ConvParams &q, int bm) {

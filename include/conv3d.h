@@ -100,6 +100,8 @@ typedef struct {
     int64_t grid;                 /* workgroups of the main kernel */
     size_t workspace_bytes;
     char kernel_name[64];         /* the main kernel's symbol stem */
+    int32_t split_tiles;          /* tiles whose K range is split over several workgroups */
+    int32_t split_pieces;         /* K-pieces per split tile (0 if none) */
 } conv3d_plan_info;
 
 /*
@@ -112,8 +114,12 @@ typedef struct {
  * not a multiple of 8, kernel extents above 7, spatial extents above 8192,
  * 2^30 or more input or output voxels, weights of 1 GiB or more, or frames
  * so large that the input rows one output tile reads span 1 GiB.
- * The environment variable CONV3D_FORCE_PATH=general behaves like
- * CONV3D_F_NO_T1_FASTPATH; CONV3D_TILE=<name> forces a tile configuration.
+ * The plan may split the K range of the tiles that do not fill a whole wave
+ * of workgroups into pieces that run concurrently and leave fp32 partial
+ * tiles in the workspace, summed by a second small kernel; the workspace then
+ * holds those partials.  The environment variable CONV3D_FORCE_PATH=general
+ * behaves like CONV3D_F_NO_T1_FASTPATH; CONV3D_TILE=<name> forces a tile
+ * configuration; CONV3D_STREAMK=0 forbids and =1 forces the K split.
  */
 conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *workspace_bytes);
 
@@ -127,8 +133,9 @@ void conv3d_plan_destroy(conv3d_plan_t p);
  * Enqueue y = conv3d(x, weight) (+bias) (+residual) on stream.
  * x, weight, y: required device pointers.  bias / residual: required when the
  * plan's flags say so, otherwise ignored.  workspace: device memory of at
- * least the planned size (may be NULL when that size is 0); its contents are
- * scratch, overwritten by each call.  Calls on different streams must not
+ * least the planned size (may be NULL when that size is 0): folded first-frame
+ * weights and/or fp32 partial tiles; its contents are scratch, overwritten by
+ * each call.  Calls on different streams must not
  * share a workspace.  y must not overlap x, weight, bias or residual.
  * Errors: INVALID_ARG (null/misaligned pointers, y aliasing an input),
  * WORKSPACE (workspace_bytes below the planned size), HIP (launch failure).

@@ -46,6 +46,29 @@ def check_guards(buf):
 
 
 @contextmanager
+def env_var(name, value):
+    old = os.environ.get(name)
+    if value is None:
+        os.environ.pop(name, None)
+    else:
+        os.environ[name] = value
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop(name, None)
+        else:
+            os.environ[name] = old
+
+
+def workspace_for(plan):
+    """Device workspace of the planned size (None when the plan needs none)."""
+    if not plan.workspace_bytes:
+        return None
+    return torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda:0")
+
+
+@contextmanager
 def forced_tile(name):
     old = os.environ.get("CONV3D_TILE")
     if name:
@@ -78,13 +101,16 @@ def out_dims(shape):
             shape.cout)
 
 
-def run_conv(shape, x, w, b=None, res=None, flags=0, tile=None, keep_device=False):
-    """Run the HIP conv through the C ABI; returns (y fp16 numpy or device tensor, plan info)."""
+def run_conv(shape, x, w, b=None, res=None, flags=0, tile=None, keep_device=False, split=None):
+    """Run the HIP conv through the C ABI; returns (y fp16 numpy or device tensor, plan info).
+
+    split: None lets the planner decide on K-splitting; "0" forbids it, "1" forces it.
+    """
     if b is not None:
         flags |= c3d.CONV3D_F_BIAS
     if res is not None:
         flags |= c3d.CONV3D_F_RESIDUAL
-    with forced_tile(tile):
+    with forced_tile(tile), env_var("CONV3D_STREAMK", split):
         plan = c3d.conv3d_plan(conv_desc(shape, flags))
     info = plan.info()
     xd = x if isinstance(x, torch.Tensor) else dev(x)
@@ -92,10 +118,7 @@ def run_conv(shape, x, w, b=None, res=None, flags=0, tile=None, keep_device=Fals
     bd = None if b is None else (b if isinstance(b, torch.Tensor) else dev(b))
     rd = None if res is None else (res if isinstance(res, torch.Tensor) else dev(res))
     buf, y = guarded_empty(out_dims(shape))
-    ws = None
-    if plan.workspace_bytes:
-        ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda:0")
-    c3d.conv3d_forward(plan, xd, wd, bd, rd, y, ws)
+    c3d.conv3d_forward(plan, xd, wd, bd, rd, y, workspace_for(plan))
     torch.cuda.synchronize()
     check_guards(buf)
     if keep_device:

@@ -91,7 +91,10 @@ def test_plan_paths_and_sizes():
     assert (i.t_out, i.h_out, i.w_out) == (9, 64, 64)
     assert (i.gemm_m, i.gemm_n, i.gemm_k) == (9 * 64 * 64, 512, 27 * 512)
     assert i.flops == 2.0 * 36864 * 512 * 13824
-    assert p.workspace_bytes == 0 and i.grid > 0
+    # the workspace holds exactly the fp32 partial tiles of any K split
+    assert p.workspace_bytes == i.split_tiles * i.split_pieces * i.tile_m * i.tile_n * 4
+    assert i.grid == (i.gemm_m + i.tile_m - 1) // i.tile_m * ((512 + i.tile_n - 1) // i.tile_n) \
+        - i.split_tiles + i.split_tiles * i.split_pieces
 
     p1 = c3d.conv3d_plan(desc(t=1))
     i1 = p1.info()
@@ -109,6 +112,23 @@ def test_plan_paths_and_sizes():
     assert pz.path == c3d.CONV3D_PATH_T1_FOLD
     pw = c3d.conv3d_plan(desc(kt=1, kh=1, kw=1, pad_t_front=0, pad_h=0, pad_w=0)).info()
     assert pw.path == c3d.CONV3D_PATH_POINTWISE and pw.gemm_k == 512
+
+
+def test_k_split_switch():
+    os.environ["CONV3D_STREAMK"] = "0"
+    try:
+        i = c3d.conv3d_plan(desc()).info()
+        assert i.split_tiles == 0 and i.split_pieces == 0
+    finally:
+        del os.environ["CONV3D_STREAMK"]
+    os.environ["CONV3D_STREAMK"] = "1"
+    try:
+        p = c3d.conv3d_plan(desc(t=3, h=10, w=13, c_in=64, c_out=72))
+        i = p.info()
+        assert i.split_tiles > 0 and i.split_pieces >= 2
+        assert p.workspace_bytes >= i.split_tiles * i.split_pieces * i.tile_m * i.tile_n * 4
+    finally:
+        del os.environ["CONV3D_STREAMK"]
 
 
 def test_forced_tile_and_unknown_tile():
@@ -149,7 +169,7 @@ def test_forward_argument_checks():
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="host without a GPU only")
 def test_forward_without_a_device_reports_no_device():
     p = c3d.conv3d_plan(desc())
-    assert fwd(p) == c3d.CONV3D_ERR_NO_DEVICE
+    assert fwd(p, ws=A + 4096 * MB, wsb=p.workspace_bytes) == c3d.CONV3D_ERR_NO_DEVICE
 
 
 def test_groupnorm_argument_checks():

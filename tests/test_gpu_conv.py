@@ -240,3 +240,29 @@ def test_streaming_pointwise_bias_residual_bound():
     assert info.kernel_name.decode().startswith("conv1x1_stream")
     ref, mag = oracle_full(s, d["x"], d["w"], d["b"], res)
     assert_conv_close(y, ref, mag, "pointwise + residual")
+
+
+@pytest.mark.parametrize("tile", ["m256n256k64s2w8", "m256n256k64s2w4", "m256n128k64s2w4",
+                                  "m128n128k64s3w4"])
+def test_k_split_matches_whole_tiles_exactly(tile):
+    s = ConvShape(1, 3, 20, 24, 64, 96)
+    x = ternary(s.x_shape, 70)
+    w = ternary(s.w_shape, 71)
+    b = np.random.default_rng(72).integers(-2, 3, s.cout).astype(np.float16)
+    y1, info1 = run_conv(s, x, w, b, tile=tile, split="1")
+    assert info1.split_tiles > 0 and info1.split_pieces >= 2
+    y0, info0 = run_conv(s, x, w, b, tile=tile, split="0")
+    assert info0.split_tiles == 0
+    ref, _ = oracle_full(s, x, w, b)
+    assert np.array_equal(y1.astype(np.float64), ref)
+    assert np.array_equal(y0, y1)
+
+
+def test_k_split_with_residual_within_bound():
+    s = ConvShape(1, 4, 18, 20, 128, 128)
+    d = workloads.conv_inputs(s, 650)
+    res = workloads.normal_f16(np.random.SeedSequence(651), out_dims(s))
+    y, info = run_conv(s, d["x"], d["w"], d["b"], res=res, tile="m256n256k64s2w8", split="1")
+    assert info.split_tiles > 0
+    ref, mag = oracle_full(s, d["x"], d["w"], d["b"], res)
+    assert_conv_close(y, ref, mag, "split K + residual")

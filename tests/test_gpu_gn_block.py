@@ -16,7 +16,7 @@ import workloads
 from workloads import ConvShape
 
 from helpers import (assert_conv_close, assert_gn_close, check_guards, dev, edge_voxels,
-                     guarded_empty, out_dims, sample_points, conv_desc)
+                     guarded_empty, out_dims, sample_points, conv_desc, workspace_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -95,6 +95,7 @@ class Block:
         self.s, self.groups, self.eps = shape, groups, eps
         self.p1 = c3d.conv3d_plan(conv_desc(shape, c3d.CONV3D_F_BIAS))
         self.p2 = c3d.conv3d_plan(conv_desc(shape, c3d.CONV3D_F_BIAS | c3d.CONV3D_F_RESIDUAL))
+        self.ws1, self.ws2 = workspace_for(self.p1), workspace_for(self.p2)
         self.thw = shape.t * shape.h * shape.w
         need = c3d.groupnorm_silu_workspace(shape.n, self.thw, shape.cin, groups)
         self.ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
@@ -107,10 +108,10 @@ class Block:
         out = torch.empty_like(c1)
         c3d.groupnorm_silu(x, p["gamma1"], p["beta1"], a1, s.n, self.thw, s.cin, self.groups,
                            self.eps, True, self.ws)
-        c3d.conv3d_forward(self.p1, a1, p["w1"], p["b1"], None, c1)
+        c3d.conv3d_forward(self.p1, a1, p["w1"], p["b1"], None, c1, self.ws1)
         c3d.groupnorm_silu(c1, p["gamma2"], p["beta2"], a2, s.n, self.thw, s.cout, self.groups,
                            self.eps, True, self.ws)
-        c3d.conv3d_forward(self.p2, a2, p["w2"], p["b2"], x, out)
+        c3d.conv3d_forward(self.p2, a2, p["w2"], p["b2"], x, out, self.ws2)
         return a1, c1, a2, out
 
 
