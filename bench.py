@@ -134,6 +134,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall seconds of oracle work for cpu_baseline (0 disables it)")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel extras")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with one 1 GiB device-to-device copy (scales byte counters in profiles)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -297,6 +299,12 @@ def main():
         result["cpu_baseline"] = cpu_baseline_leg(d1, y.cpu().numpy(), info, args.cpu_seconds, np)
     else:
         result["cpu_baseline"] = None
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        torch.empty_like(a).copy_(a)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = 1 << 30
 
     print(json.dumps(result), flush=True)
 
