@@ -129,8 +129,9 @@ def cpu_baseline_leg(d, y_dev, info, target_s, np):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first; the clocks need ~50 ms of load to settle")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall seconds of oracle work for cpu_baseline (0 disables it)")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel extras")

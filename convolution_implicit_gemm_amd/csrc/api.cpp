@@ -80,7 +80,7 @@ struct Decomp {
     double seconds;
 };
 
-constexpr double kBestRatePerCU = 1130e12 / kCUs;  // flop/s of the best tile config, per CU
+constexpr double kBestRatePerCU = 1220e12 / kCUs;  // flop/s of the best tile config, per CU
 constexpr double kFixupBytesPerSec = 4.5e12;
 constexpr double kLaunchSeconds = 4e-6;
 constexpr size_t kMaxSplitWorkspace = (size_t)256 << 20;

@@ -21,7 +21,7 @@ struct ConvParams {
     int32_t To, Ho, Wo;
     int32_t kt, kh, kw, ptf, ph, pw, replicate;
     int32_t K;             // kt*kh*kw*Cin
-    int32_t cpt;           // K-iterations per tap: ceil(Cin / BK)
+    int32_t cpt;           // channel slices: ceil(Cin / BK); the K loop is slice-major, taps fastest
     int32_t niter;         // kt*kh*kw*cpt
     int32_t m_tiles, n_tiles;
     int32_t dp_tiles;      // tiles [0, dp_tiles) run whole, one workgroup each

@@ -29,14 +29,23 @@
 //    index.  Rows past M, channels past Cout and (tail variant) channels past
 //    Cin use the same out-of-range offset.  Each tile addresses its own window
 //    of the input (a buffer resource based at the lowest voxel it can touch),
-//    so 32-bit offsets suffice for multi-GB tensors.  Walking along K inside a
-//    tap only moves the scalar offset.
-//  * STAGES-deep ring of LDS buffers; one s_waitcnt vmcnt(N) + s_barrier per
+//    so 32-bit offsets suffice for multi-GB tensors.
+//  * The K loop runs channel-chunk-major: for one BK-wide slice of the input
+//    channels it visits every tap (tau, r, s) before moving to the next slice.
+//    Consecutive taps re-read the same input voxels shifted by one voxel, row
+//    or frame, so the slice of the input window that the tiles running on one
+//    XCD touch (about 2-4 MB) is re-read from L2 instead of from HBM.  The
+//    weight columns of a (tap, slice) pair are a scalar offset away.
+//  * Rings of LDS buffers, one for weights and one for activations (the
+//    activation ring may be one buffer deeper, so the operand that misses L2
+//    is fetched a K-iteration earlier); one s_waitcnt vmcnt(N) + s_barrier per
 //    K-iteration.  __syncthreads() is avoided on purpose: its release fence
 //    waits for every outstanding load, which would drain the prefetch ring.
 //  * Workgroups are renumbered so each XCD (workgroup id mod 8) walks a
 //    contiguous range of tiles; tiles sharing input rows then share an L2.
 #include "c3d_internal.h"
+
+#include <type_traits>
 
 namespace c3d {
 
@@ -46,10 +55,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 1: pin the MFMA / LDS-read / load interleave with sched_group_barrier.
-#ifndef C3D_SCHED
-#define C3D_SCHED 0
-#endif
+
+// Calls f(std::integral_constant<int, i>{}) for i = 0..N-1 (compile-time indices).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
 
 // Bank swizzle of 16-byte chunks within an LDS row of BK halves.  Chosen so
 // that 32 consecutive rows read at one logical chunk by ds_read_b128 hit
@@ -153,7 +167,12 @@ __device__ __forceinline__ void store_tile(const ConvParams &p, const f32x16 (&a
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool TAIL>
+// STAGES: depth of the weight ring; ASTAGES (STAGES or STAGES + 1): depth of
+// the activation ring.  With one more activation buffer the gathered input,
+// the operand that misses L2, is fetched one K-iteration further ahead than
+// the weights, which every tile on an XCD reads at about the same time.
+// TT: kt <= 3, gather offsets from per-tile tables (see set_offsets).
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int ASTAGES, bool TAIL, bool TT>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kernel(ConvParams p) {
     constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN;
     constexpr int RB = BK * 2;        // bytes per LDS row
@@ -163,13 +182,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
     constexpr int QB = BN / RPI;      // weight load instructions per stage
     constexpr int LA = (QA + NW - 1) / NW, LB = (QB + NW - 1) / NW;
     constexpr int TM = WM / 32, TN = WN / 32, KS = BK / 16;
-    constexpr int B_OFF = BN * RB;                  // activations follow the weights
-    constexpr int STAGE_BYTES = (BM + BN) * RB;
+    constexpr int D = ASTAGES - STAGES;            // activation lead, in stages
+    constexpr int W_BYTES = BN * RB, A_BYTES = BM * RB;
+    constexpr int A_RING = STAGES * W_BYTES;       // the activation ring follows the weight ring
+    constexpr int LDS_BYTES = STAGES * W_BYTES + ASTAGES * A_BYTES;
+    static_assert(D == 0 || D == 1, "activation ring: STAGES or STAGES + 1 buffers");
+    static_assert(STAGES >= 2, "double buffering at least");
     static_assert(BM % RPI == 0 && BN % RPI == 0, "tile rows must fill whole load instructions");
-    static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS is 160 KiB per CU");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS is 160 KiB per CU");
     static_assert(KS >= 2, "two k-steps per stage at least");
 
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -229,6 +252,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
     const int lrow = lane / CPR, lchunk = lane % CPR;
     const int cin2 = Cin * 2;
     int a_t[LA], a_h[LA], a_w[LA], a_base[LA], a_c2[LA];
+    // TT: byte offset (in the tile's window) of the source voxel at temporal
+    // tap 0 and spatial offset (0, 0), the steps to taps 1 and 2, and a mask
+    // of the taps that read inside the input: bit s, bit 8 + r, bit 16 + tau.
+    uint32_t a_tb0[LA], a_d1[LA], a_d2[LA], a_ok[LA];
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
         const int row = (j * NW + wv) * RPI + lrow;
@@ -241,11 +268,29 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
             a_h[j] = ho;
             a_w[j] = wo;
             a_base[j] = vb - lo - to * HW;  // + ts*HW + tap offset = source voxel - lo
+            if constexpr (TT) {
+                uint32_t tb[3], ok = 0;
+#pragma unroll
+                for (int tau = 0; tau < 3; ++tau) {
+                    int ts = to + tau - p.ptf;
+                    const bool inside = (unsigned)ts < (unsigned)T;
+                    if (p.replicate) ts = ts < 0 ? 0 : (ts > T - 1 ? T - 1 : ts);
+                    tb[tau] = (uint32_t)(a_base[j] + ts * HW) * (uint32_t)cin2 + (uint32_t)a_c2[j];
+                    ok |= (uint32_t)(tau < p.kt && (inside || p.replicate)) << (16 + tau);
+                }
+                for (int r = 0; r < p.kh; ++r) ok |= (uint32_t)((unsigned)(ho + r - p.ph) < (unsigned)H) << (8 + r);
+                for (int q = 0; q < p.kw; ++q) ok |= (uint32_t)((unsigned)(wo + q - p.pw) < (unsigned)W) << q;
+                a_tb0[j] = tb[0];
+                a_d1[j] = tb[1] - tb[0];
+                a_d2[j] = tb[2] - tb[1];
+                a_ok[j] = ok;
+            }
         } else {
             a_t[j] = 0;
             a_h[j] = 1 << 20;  // never inside [0, H): the row reads zeros
             a_w[j] = 0;
             a_base[j] = 0;
+            a_tb0[j] = a_d1[j] = a_d2[j] = a_ok[j] = 0;  // no tap reads inside
         }
     }
     uint32_t b_voff[LB];
@@ -258,40 +303,55 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
         b_voff[j] = co < p.Cout ? (uint32_t)(co * p.K + b_c8[j]) * 2u : kOOB;
     }
 
-    // ---- load side: the stage being fetched is (tap = (tau, r, s), ci0).  Its
-    // per-lane offsets are recomputed branch-free every K-iteration (a few VALU
-    // per slot, interleaved with the MFMAs); K inside a tap moves only the
-    // scalar offset.  After the last stage the state freezes, so the extra
-    // fetches that keep every wave's load count constant re-read valid data
-    // into a buffer nobody reads again.
+    // ---- load side: the stage being fetched is (ci0, tap = (tau, r, s)), taps
+    // fastest.  Its per-lane offsets are recomputed branch-free every
+    // K-iteration (a few VALU per slot, interleaved with the MFMAs); the channel
+    // slice moves only the scalar offset.  After the last stage the state
+    // freezes, so the extra fetches that keep every wave's load count constant
+    // re-read valid data into a buffer nobody reads again.
     const int t_lo = p.replicate ? 0 : -(1 << 20), t_hi = p.replicate ? T - 1 : (1 << 20);
-    int ld_it = it0, ld_ci = (it0 % p.cpt) * BK, ld_tap = it0 / p.cpt;
+    const int ntaps = p.kt * p.kh * p.kw;
+    int ld_it = it0, ld_ci = (it0 / ntaps) * BK, ld_tap = it0 % ntaps;
     int ld_s = ld_tap % p.kw, ld_r = (ld_tap / p.kw) % p.kh, ld_tau = ld_tap / (p.kw * p.kh);
     uint32_t a_voff[LA];
     auto set_offsets = [&]() {
         const int dr = ld_r - p.ph, ds = ld_s - p.pw;
         const int dt = ld_tau - p.ptf;
         const int rs = dr * W + ds;
+        if constexpr (TT) {
+            // a few full-rate VALU per slot: two masked steps (tau >= 1, >= 2),
+            // the spatial byte offset (scalar) and the tap's validity bits
+            const uint32_t sel = (1u << ld_s) | (1u << (8 + ld_r)) | (1u << (16 + ld_tau));
+            const uint32_t m1 = ld_tau >= 1 ? ~0u : 0u, m2 = ld_tau >= 2 ? ~0u : 0u;
+            const uint32_t rsc = (uint32_t)rs * (uint32_t)cin2;
 #pragma unroll
-        for (int j = 0; j < LA; ++j) {
-            int ts = a_t[j] + dt;
-            ts = ts < t_lo ? t_lo : (ts > t_hi ? t_hi : ts);  // clamp only when replicating
-            const bool ok = ((unsigned)ts < (unsigned)T) & ((unsigned)(a_h[j] + dr) < (unsigned)H) &
-                            ((unsigned)(a_w[j] + ds) < (unsigned)W);
-            const int rel = a_base[j] + ts * HW + rs;
-            // valid offsets are below 2^30 (the plan bounds every tile's window);
-            // invalid ones land in [2^31, 2^31 + 2^30): past the records, and
-            // far enough from 2^32 that adding the scalar offset cannot wrap.
-            // Arithmetic rather than a select, which the compiler would turn
-            // into an exec-masked block around the multiply.
-            a_voff[j] = (((uint32_t)rel * (uint32_t)cin2 + (uint32_t)a_c2[j]) & 0x3FFFFFFFu) |
-                        ((uint32_t)!ok << 31);
+            for (int j = 0; j < LA; ++j) {
+                const uint32_t off = a_tb0[j] + (a_d1[j] & m1) + (a_d2[j] & m2) + rsc;
+                a_voff[j] = (a_ok[j] & sel) == sel ? off : kOOB;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < LA; ++j) {
+                int ts = a_t[j] + dt;
+                ts = ts < t_lo ? t_lo : (ts > t_hi ? t_hi : ts);  // clamp only when replicating
+                const bool ok = ((unsigned)ts < (unsigned)T) & ((unsigned)(a_h[j] + dr) < (unsigned)H) &
+                                ((unsigned)(a_w[j] + ds) < (unsigned)W);
+                const int rel = a_base[j] + ts * HW + rs;
+                // valid offsets are below 2^30 (the plan bounds every tile's
+                // window); invalid ones land in [2^31, 2^31 + 2^30): past the
+                // records, and far enough from 2^32 that adding the scalar
+                // offset cannot wrap.  Arithmetic rather than a select, which
+                // the compiler would turn into an exec-masked block around the
+                // multiply.
+                a_voff[j] = (((uint32_t)rel * (uint32_t)cin2 + (uint32_t)a_c2[j]) & 0x3FFFFFFFu) |
+                            ((uint32_t)!ok << 31);
+            }
         }
     };
-    auto fire = [&](int buf) {
-        char *sb = smem + buf * STAGE_BYTES;
+    // weights of the stage at the cursor into weight buffer wbuf
+    auto fire_w = [&](int wbuf) {
+        char *sb = smem + wbuf * W_BYTES;
         const uint32_t s_w = (uint32_t)(ld_tap * Cin + ld_ci) * 2u;
-        const uint32_t s_a = (uint32_t)ld_ci * 2u;
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
             const int q = j * NW + wv;
@@ -300,35 +360,49 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
                 dma16(wr, sb + q * 1024, v, s_w);
             }
         }
+    };
+    // activations of the stage at the cursor (offsets from set_offsets) into
+    // activation buffer abuf; PART < 0: every load, else only the loads that
+    // belong to k-step PART when the fetch is spread over KS - 1 k-steps
+    auto fire_a = [&](int abuf, auto part) {
+        constexpr int PART = decltype(part)::value;
+        char *sb = smem + A_RING + abuf * A_BYTES;
+        const uint32_t s_a = (uint32_t)ld_ci * 2u;
 #pragma unroll
         for (int j = 0; j < LA; ++j) {
             const int q = j * NW + wv;
+            if constexpr (PART >= 0) {
+                if (j * (KS - 1) / LA != PART) continue;
+            }
             if (QA % NW == 0 || q < QA) {
                 const uint32_t v = (!TAIL || ld_ci + a_c2[j] / 2 < Cin) ? a_voff[j] : kOOB;
-                dma16(xr, sb + B_OFF + q * 1024, v, s_a);
+                dma16(xr, sb + q * 1024, v, s_a);
             }
         }
-        // advance (tau, r, s, ci0) with selects only; freeze after the last stage
+    };
+    // advance the cursor (ci0, tau, r, s) with selects only; freeze after the
+    // last stage
+    auto advance = [&]() {
         const int step = ld_it + 1 < it1 ? 1 : 0;
         ++ld_it;
-        const int nci = ld_ci + BK * step;
-        const int wrap = nci >= Cin ? 1 : 0;
-        ld_ci = wrap ? 0 : nci;
-        ld_tap += wrap;
-        const int ns = ld_s + wrap;
+        const int ns = ld_s + step;
         const int wrap_s = ns == p.kw ? 1 : 0;
         ld_s = wrap_s ? 0 : ns;
         const int nr = ld_r + wrap_s;
         const int wrap_r = nr == p.kh ? 1 : 0;
         ld_r = wrap_r ? 0 : nr;
-        ld_tau += wrap_r;
+        const int nt = ld_tau + wrap_r;
+        const int wrap_t = nt == p.kt ? 1 : 0;
+        ld_tau = wrap_t ? 0 : nt;
+        ld_tap = wrap_t ? 0 : ld_tap + step;
+        ld_ci += BK * wrap_t;
     };
 
     // ---- per-lane LDS read offsets for the MFMA fragments
     const int rrow = lane & 31, rhi = lane >> 5;
     const int wmi = wv / NWN, wni = wv % NWN;
     const int a_frag0 = wni * WN * RB;              // weights (MFMA A)
-    const int b_frag0 = B_OFF + wmi * WM * RB;      // activations (MFMA B)
+    const int b_frag0 = A_RING + wmi * WM * RB;     // activations (MFMA B)
     int koff[KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) koff[kk] = rrow * RB + (((2 * kk + rhi) ^ swz<BK>(rrow)) * 16);
@@ -342,13 +416,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     half8_t af[2][TN], bf[2][TM];
-    auto read_frags = [&](const char *sb, int kk, int slot) {
+    // fragments of k-step kk from weight buffer wbuf and activation buffer abuf
+    auto read_frags = [&](int wbuf, int abuf, int kk, int slot) {
+        const char *wsb = smem + wbuf * W_BYTES;
+        const char *asb = smem + abuf * A_BYTES;
 #pragma unroll
         for (int i = 0; i < TN; ++i)
-            af[slot][i] = *reinterpret_cast<const half8_t *>(sb + a_frag0 + i * 32 * RB + koff[kk]);
+            af[slot][i] = *reinterpret_cast<const half8_t *>(wsb + a_frag0 + i * 32 * RB + koff[kk]);
 #pragma unroll
         for (int j = 0; j < TM; ++j)
-            bf[slot][j] = *reinterpret_cast<const half8_t *>(sb + b_frag0 + j * 32 * RB + koff[kk]);
+            bf[slot][j] = *reinterpret_cast<const half8_t *>(asb + b_frag0 + j * 32 * RB + koff[kk]);
     };
     auto mfmas = [&](int slot) {
 #pragma unroll
@@ -358,49 +435,58 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[slot][i], bf[slot][j], acc[i][j], 0, 0, 0);
     };
 
-    // Loads per wave per stage.  Waves may differ by one instruction when a
-    // tile's rows do not split evenly over the waves; waiting for "at most
-    // STAGES-1 stages of the smallest count" in flight still guarantees, on
-    // every wave, that its oldest stage has landed.
-    constexpr int LOADS = QA / NW + QB / NW;
-    constexpr int READS = TN + TM, MF = TN * TM;
+    // Fetch schedule.  Stage k's activations and weights are fetched while
+    // stage k - STAGES is computed: with D = 0 both at its barrier (when the
+    // buffers of stage k - STAGES fall free); with D = 1 the activations go to
+    // the extra buffer, spread over the k-steps before that barrier, and only
+    // the weights at the barrier.  Issuing all of a stage's loads at once
+    // stalls every wave's in-order issue behind the address unit.
+    //
+    // Loads per wave per stage may differ by one instruction between waves when
+    // a tile's rows do not split evenly; the waits count the smallest number,
+    // which on every wave still covers the stage waited for (loads return in
+    // issue order).  Before the first k-step everything after stage 0 may stay
+    // in flight; at the loop's barrier everything after stage it+1: the
+    // (STAGES-2) later whole stages, plus with D = 1 the activations of stage
+    // it+STAGES issued in this iteration.
+    constexpr int LW = QB / NW, LAm = QA / NW;
+    constexpr int WAIT_FIRST = (STAGES - 1) * (LW + LAm);
+    constexpr int WAIT_LOOP = (STAGES - 2) * (LW + LAm) + D * LAm;
+    using all_loads = std::integral_constant<int, -1>;
 
-    // prologue: fill every buffer, wait for stage 0, read its first k-step
+    // prologue: stages 0..STAGES-1, wait for stage 0, read its first k-step
 #pragma unroll
     for (int s = 0; s < STAGES; ++s) {
         set_offsets();
-        fire(s);
+        fire_a(s, all_loads{});
+        fire_w(s);
+        advance();
     }
-    wait_lds_and_loads<(STAGES - 1) * LOADS>();
-    read_frags(smem, 0, 0);
+    set_offsets();
+    wait_lds_and_loads<WAIT_FIRST>();
+    read_frags(0, 0, 0, 0);
 
+    int wbuf = 0, abuf = 0;  // buffers of stage it
+    int afill = STAGES % ASTAGES;  // D = 1: buffer of stage it+STAGES
     for (int it = it0; it < it1; ++it) {
-        const int buf = (it - it0) % STAGES;
-        const char *sb = smem + buf * STAGE_BYTES;
-        // region A: k-steps 0..KS-2 of this stage; offsets of the next fetch
-#pragma unroll
-        for (int kk = 0; kk < KS - 1; ++kk) {
-            read_frags(sb, kk + 1, (kk + 1) & 1);
+        // region A: k-steps 1..KS-1 of this stage are read, 0..KS-2 multiplied
+        static_for<KS - 1>([&](auto kk) {
+            read_frags(wbuf, abuf, kk + 1, (kk + 1) & 1);
+            if constexpr (D == 1) fire_a(afill, kk);
             mfmas(kk & 1);
-        }
-        set_offsets();
-        if constexpr (C3D_SCHED) {
-            constexpr int NM = (KS - 1) * MF, ND = (KS - 1) * READS;
-            constexpr int GAP = NM / ND > 0 ? NM / ND : 1;
-#pragma unroll
-            for (int q = 0; q < NM; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
-                if (q % GAP == 0 && q / GAP < ND)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);      // a few VALU
-            }
-        }
+        });
         // stage it+1 has landed and every wave is done reading stage it
-        wait_lds_and_loads<(STAGES - 2) * LOADS>();
-        // region B: refill this stage's buffer, read k-step 0 of the next stage,
-        // and run the last k-step of this one meanwhile
-        fire(buf);
-        read_frags(smem + ((it - it0 + 1) % STAGES) * STAGE_BYTES, 0, 0);
+        wait_lds_and_loads<WAIT_LOOP>();
+        // region B: refill this stage's buffers, read k-step 0 of the next
+        // stage, and run the last k-step of this one meanwhile
+        if constexpr (D == 0) fire_a(abuf, all_loads{});
+        fire_w(wbuf);
+        advance();
+        set_offsets();
+        if constexpr (D == 1) afill = abuf;
+        wbuf = wbuf + 1 == STAGES ? 0 : wbuf + 1;
+        abuf = abuf + 1 == ASTAGES ? 0 : abuf + 1;
+        read_frags(wbuf, abuf, 0, 0);
         mfmas((KS - 1) & 1);
     }
     wait_lds_and_loads<0>();  // drain the extra fetches before LDS is released
@@ -462,11 +548,16 @@ __global__ __launch_bounds__(256) void conv3d_fixup_kernel(ConvParams p) {
     *reinterpret_cast<half4_t *>(p.y + o) = h;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool TAIL>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int ASTAGES, bool TAIL>
 hipError_t launch_igemm(const ConvParams &p, hipStream_t s) {
     constexpr int threads = (BM / WM) * (BN / WN) * 64;
     const unsigned grid = (unsigned)(p.dp_tiles + p.sk_tiles * p.sk_pieces);
-    hipLaunchKernelGGL((conv3d_igemm_kernel<BM, BN, BK, WM, WN, STAGES, TAIL>), dim3(grid), dim3(threads), 0, s, p);
+    if (p.kt <= 3)
+        hipLaunchKernelGGL((conv3d_igemm_kernel<BM, BN, BK, WM, WN, STAGES, ASTAGES, TAIL, true>), dim3(grid),
+                           dim3(threads), 0, s, p);
+    else
+        hipLaunchKernelGGL((conv3d_igemm_kernel<BM, BN, BK, WM, WN, STAGES, ASTAGES, TAIL, false>), dim3(grid),
+                           dim3(threads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -479,20 +570,23 @@ hipError_t launch_fixup(const ConvParams &p, hipStream_t s) {
 }
 
 // rate: throughput per CU relative to the best configuration, measured on a
-// full-wave workload (causal 3x3x3, 512 -> 256, 256x256 frames)
-#define C3D_TILE(NAME, BM, BN, BK, WM, WN, ST, RATE)                                            \
-    {NAME, BM, BN, BK, ST, (BM / WM) * (BN / WN) * 64, (size_t)(ST) * ((BM) + (BN)) * (BK) * 2, \
-     RATE, launch_igemm<BM, BN, BK, WM, WN, ST, false>, launch_igemm<BM, BN, BK, WM, WN, ST, true>, \
+// full-wave workload (causal 3x3x3, 512 -> 256, 256x256 frames).  ST / AST:
+// weight / activation ring depth.
+#define C3D_TILE(NAME, BM, BN, BK, WM, WN, ST, AST, RATE)                                            \
+    {NAME, BM, BN, BK, ST, (BM / WM) * (BN / WN) * 64, (size_t)((ST) * (BN) + (AST) * (BM)) * (BK) * 2, \
+     RATE, launch_igemm<BM, BN, BK, WM, WN, ST, AST, false>, launch_igemm<BM, BN, BK, WM, WN, ST, AST, true>, \
      launch_fixup<BM, BN, WM, WN>}
 
 static const TileCfg k_tiles[] = {
-    C3D_TILE("m256n256k64s2w4", 256, 256, 64, 128, 128, 2, 0.93),
-    C3D_TILE("m256n256k32s4w4", 256, 256, 32, 128, 128, 4, 0.89),
-    C3D_TILE("m256n256k64s2w8", 256, 256, 64, 64, 128, 2, 1.00),
-    C3D_TILE("m256n128k64s2w4", 256, 128, 64, 128, 64, 2, 0.83),
-    C3D_TILE("m128n128k64s3w4", 128, 128, 64, 64, 64, 3, 0.72),
-    C3D_TILE("m128n64k64s2w4", 128, 64, 64, 32, 64, 2, 0.68),
-    C3D_TILE("m128n32k32s2w4", 128, 32, 32, 32, 32, 2, 0.31),
+    C3D_TILE("m256n256k64s2w4", 256, 256, 64, 128, 128, 2, 2, 0.91),
+    C3D_TILE("m256n256k32s4w4", 256, 256, 32, 128, 128, 4, 4, 0.85),
+    C3D_TILE("m256n256k64s2w8", 256, 256, 64, 64, 128, 2, 2, 0.96),
+    C3D_TILE("m256n256k64s2a3w8", 256, 256, 64, 64, 128, 2, 3, 1.00),
+    C3D_TILE("m256n256k64s2a3w4", 256, 256, 64, 128, 128, 2, 3, 0.94),
+    C3D_TILE("m256n128k64s2w4", 256, 128, 64, 128, 64, 2, 2, 0.80),
+    C3D_TILE("m128n128k64s3w4", 128, 128, 64, 64, 64, 3, 3, 0.69),
+    C3D_TILE("m128n64k64s2w4", 128, 64, 64, 32, 64, 2, 2, 0.65),
+    C3D_TILE("m128n32k32s2w4", 128, 32, 32, 32, 32, 2, 2, 0.30),
 };
 
 int64_t tile_window_voxels(const ConvParams &q, int bm) {

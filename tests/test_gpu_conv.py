@@ -42,6 +42,9 @@ def test_library_loads_on_gpu():
 EXACT_CASES = [
     ConvShape(2, 3, 10, 13, 64, 72),                                     # causal replicate
     ConvShape(2, 3, 10, 13, 40, 72, pad_t_front=1, pad_t_back=1, tmode=Z),  # zero, channel tail
+    # three K-iterations: fewer than the load rings are deep
+    ConvShape(1, 2, 7, 9, 64, 40, kt=1, kh=1, kw=3, pad_t_front=0, pad_t_back=0, pad_h=0, pad_w=1,
+              tmode=Z),
 ]
 
 
@@ -55,6 +58,21 @@ def test_ternary_bit_exact_every_tile(tile, case):
     y, info = run_conv(s, x, w, b, tile=tile)
     assert info.kernel_name.decode().startswith("conv3d_igemm_" + tile)
     ref, _ = oracle_full(s, x, w, b)
+    assert np.array_equal(y.astype(np.float64), ref), tile
+
+
+@pytest.mark.parametrize("tile", tile_names())
+def test_single_k_iteration_every_tile(tile):
+    # a 1x1x1 conv on a forced implicit-GEMM tile (instead of the streaming
+    # kernel): one K-iteration, so every prefetch past the first re-reads the
+    # frozen last stage
+    s = ConvShape(1, 2, 5, 6, 64, 32, kt=1, kh=1, kw=1, pad_t_front=0, pad_t_back=0, pad_h=0,
+                  pad_w=0, tmode=Z)
+    x = ternary(s.x_shape, 40)
+    w = ternary(s.w_shape, 41)
+    y, info = run_conv(s, x, w, tile=tile)
+    assert info.kernel_name.decode().startswith("conv3d_igemm_" + tile)
+    ref, _ = oracle_full(s, x, w)
     assert np.array_equal(y.astype(np.float64), ref), tile
 
 
@@ -242,8 +260,8 @@ def test_streaming_pointwise_bias_residual_bound():
     assert_conv_close(y, ref, mag, "pointwise + residual")
 
 
-@pytest.mark.parametrize("tile", ["m256n256k64s2w8", "m256n256k64s2w4", "m256n128k64s2w4",
-                                  "m128n128k64s3w4"])
+@pytest.mark.parametrize("tile", ["m256n256k64s2w8", "m256n256k64s2a3w8", "m256n256k64s2a3w4",
+                                  "m256n256k64s2w4", "m256n128k64s2w4", "m128n128k64s3w4"])
 def test_k_split_matches_whole_tiles_exactly(tile):
     s = ConvShape(1, 3, 20, 24, 64, 96)
     x = ternary(s.x_shape, 70)
