@@ -294,16 +294,13 @@ conv3d_status conv3d_plan_query(conv3d_plan_t p, conv3d_plan_info *info) {
     info->flops = p->flops;
     info->workspace_bytes = p->ws_bytes;
     if (p->streaming) {
-        const int bm = c3d::kPointwiseRowsPerTile(p->prm.Cin);
-        const int64_t ntiles = (p->prm.M + bm - 1) / bm;
-        info->tile_m = bm;
+        const c3d::PwGeom g = c3d::pointwise_geometry(p->prm.Cin, p->prm.Cout, p->prm.M);
+        info->tile_m = g.rows;
         info->tile_n = 128;
         info->tile_k = p->prm.Cin;
-        info->stages = 2;
+        info->stages = g.ring;
         info->threads = 256;
-        const int lds = 2 * bm * p->prm.Cin * 2 + 4 * bm * 64;
-        const int per_cu = (160 * 1024 / lds) < 4 ? (160 * 1024 / lds) : 4;
-        info->grid = (ntiles < 256 * per_cu ? ntiles : 256 * per_cu) * ((p->prm.Cout + 127) / 128);
+        info->grid = g.grid_x * g.grid_y;
         snprintf(info->kernel_name, sizeof(info->kernel_name), "conv1x1_stream_cin%d", p->prm.Cin);
         return ok();
     }

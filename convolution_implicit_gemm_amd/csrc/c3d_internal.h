@@ -65,7 +65,14 @@ struct PwParams {
 };
 bool pointwise_supported(int32_t cin, int32_t cout);
 hipError_t launch_pointwise(const PwParams &p, hipStream_t s);
-constexpr int kPointwiseRowsPerTile(int) { return 64; }
+// Launch shape of the streaming kernel (reported by plan queries).
+struct PwGeom {
+    int rows;        // voxels per tile
+    int ring;        // LDS ring depth, in tiles
+    int64_t grid_x;  // persistent blocks along the voxels
+    int64_t grid_y;  // blocks of 128 output channels
+};
+PwGeom pointwise_geometry(int32_t cin, int32_t cout, int64_t m);
 
 // Sum of the temporal taps tau in [tau_lo, tau_hi] of w [Cout][kt][khw*Cin]
 // into w2 [Cout][khw*Cin], in fp32, rounded once to fp16.

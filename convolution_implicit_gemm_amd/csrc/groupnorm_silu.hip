@@ -8,16 +8,19 @@
 //          one group) of consecutive voxels, so a block reads one contiguous
 //          range.  The thread count is a multiple of C/8, so each thread keeps
 //          one group and accumulates in registers with the shifted-data
-//          method (sums of x-K and (x-K)^2 about its first value K, fp32),
+//          method (sums of x-K and (x-K)^2 about its first value K, fp32;
+//          eight 16-byte loads in flight, left in the MALL for the apply
+//          pass),
 //          then the block merges threads of a group (Chan's pairwise
 //          update) and writes (count, mean, M2) partials.
 //  final:  grid (G, N), one block per (sample, group): every thread loads its
-//          share of the SB partials at once, merges them, and the block
+//          share of the group's SB partials (one contiguous run), merges them, and the block
 //          reduces (shuffles, then LDS) to the group's mean and rstd; it
 //          writes per-channel scale a = gamma*rstd and shift b = beta - mean*a.
 //  apply:  grid (AB, N).  Each thread owns one channel vector, keeps its 8
 //          scales/shifts in registers, and streams y = x*a + b, then
-//          y*sigmoid(y), rounded once to fp16.
+//          y*sigmoid(y), rounded once to fp16, with the next batch of loads
+//          in flight while a batch is converted.
 #include "c3d_internal.h"
 
 namespace c3d {
@@ -30,36 +33,44 @@ constexpr int kMaxThreads = 1024;
 
 struct GnGeom {
     int vpv;        // 16-byte vectors per voxel (C/8)
-    int threads;    // stats/apply block size: a multiple of vpv
+    int sthreads;   // stats block size: a multiple of vpv
+    int athreads;   // apply block size: a multiple of vpv
     int sb;         // stats blocks per sample
     int ab;         // apply blocks per sample
 };
 
+// Smallest multiple of vpv that is at least `least` threads (and a multiple of
+// 64 where that fits in a block).
+int gn_block(int vpv, int least) {
+    int t = vpv;
+    while (t < least && t + vpv <= kMaxThreads) t += vpv;
+    int t64 = t;
+    while (t64 % 64 && t64 + vpv <= kMaxThreads) t64 += vpv;
+    return (t64 % 64 == 0) ? t64 : t;
+}
+
 GnGeom gn_geom(int32_t n, int64_t thw, int32_t c) {
     GnGeom g;
     g.vpv = c / 8;
-    // a multiple of vpv (one channel vector per thread), of 64 where that fits
-    // in a block, and at least 256 threads where vpv allows
-    int t = g.vpv;
-    while (t < 256 && t + g.vpv <= kMaxThreads) t += g.vpv;
-    int t64 = t;
-    while (t64 % 64 && t64 + g.vpv <= kMaxThreads) t64 += g.vpv;
-    g.threads = (t64 % 64 == 0) ? t64 : t;
-    const int vox_per_pass = g.threads / g.vpv;
-    // about 2048 stats blocks over the whole tensor, each at least 4 passes deep
-    int64_t want = (2048 + n - 1) / n;
-    int64_t maxb = (thw + 4 * vox_per_pass - 1) / (4 * vox_per_pass);
+    // stats: about 512 large blocks over the whole tensor (fewer partials for
+    // the merge), each at least 4 passes deep; apply: about 2048 blocks
+    g.sthreads = gn_block(g.vpv, 512);
+    g.athreads = gn_block(g.vpv, 256);
+    const int svox = g.sthreads / g.vpv, avox = g.athreads / g.vpv;
+    int64_t want = (512 + n - 1) / n;
+    int64_t maxb = (thw + 4 * svox - 1) / (4 * svox);
     g.sb = (int)(want < maxb ? want : maxb);
     if (g.sb < 1) g.sb = 1;
     int64_t wanta = (2048 + n - 1) / n;
-    int64_t maxa = (thw + 4 * vox_per_pass - 1) / (4 * vox_per_pass);
+    int64_t maxa = (thw + 4 * avox - 1) / (4 * avox);
     g.ab = (int)(wanta < maxa ? wanta : maxa);
     if (g.ab < 1) g.ab = 1;
     return g;
 }
 
 // Workspace layout (bytes): scale/shift [N][C] float x2 from 0; then
-// partials [N][SB][G] float4 (count, mean, M2, unused), 256-byte aligned.
+// partials [N][G][SB] float4 (count, mean, M2, unused), 256-byte aligned, so
+// that the merge of one group reads one contiguous run.
 size_t off_part(int32_t n, int32_t c) {
     size_t b = (size_t)n * c * 2 * sizeof(float);
     return (b + 255) & ~(size_t)255;
@@ -96,41 +107,32 @@ __global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(const _Float16 *_
     const int64_t v_begin = thw * b / sb, v_end = thw * (b + 1) / sb;
     const half8_t *xs = reinterpret_cast<const half8_t *>(x + (size_t)n * thw * c);
 
-    // shifted-data accumulation about the first value this thread sees
-    float K = 0.0f, s1 = 0.0f, s2 = 0.0f, cnt = 0.0f;
-    bool have_k = false;
+    // shifted-data accumulation about the first value K this thread reads.
+    // Plain (temporal) loads: the apply pass re-reads x right after, and
+    // these loads leave it in the MALL.
+    float s1 = 0.0f, s2 = 0.0f, cnt = 0.0f;
     int64_t v = v_begin + tid / vpv;
-    // four loads in flight per iteration
-    for (; v + 3 * vox_step < v_end; v += 4 * vox_step) {
-        half8_t h[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) h[u] = __builtin_nontemporal_load(xs + (v + u * vox_step) * vpv + vi);
-        if (!have_k) {
-            K = (float)h[0][0];
-            have_k = true;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float d = (float)h[u][q] - K;
-                s1 += d;
-                s2 = fmaf(d, d, s2);
-            }
-        cnt += 32.0f;
-    }
-    for (; v < v_end; v += vox_step) {
-        const half8_t h = __builtin_nontemporal_load(xs + v * vpv + vi);
-        if (!have_k) {
-            K = (float)h[0];
-            have_k = true;
-        }
+    const float K = v < v_end ? (float)xs[v * vpv + vi][0] : 0.0f;
+    auto accumulate = [&](const half8_t h) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const float d = (float)h[q] - K;
             s1 += d;
             s2 = fmaf(d, d, s2);
         }
+    };
+    // eight loads in flight per iteration
+    constexpr int U = 8;
+    for (; v + (U - 1) * vox_step < v_end; v += U * vox_step) {
+        half8_t h[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) h[u] = xs[(v + u * vox_step) * vpv + vi];
+#pragma unroll
+        for (int u = 0; u < U; ++u) accumulate(h[u]);
+        cnt += 8.0f * U;
+    }
+    for (; v < v_end; v += vox_step) {
+        accumulate(xs[v * vpv + vi]);
         cnt += 8.0f;
     }
     Welford w;
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(const _Float16 *_
                 acc = chan_merge(acc, Welford{e.x, e.y, e.z});
             }
         }
-        part[((size_t)n * sb + b) * groups + g] = make_float4(acc.n, acc.mean, acc.m2, 0.0f);
+        part[((size_t)n * groups + g) * sb + b] = make_float4(acc.n, acc.mean, acc.m2, 0.0f);
     }
 }
 
@@ -185,19 +187,19 @@ __global__ __launch_bounds__(kFinalThreads) void gn_final_kernel(const float4 *_
     __shared__ float2 stat;
     const int g = blockIdx.x, n = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float4 *p = part + (size_t)n * sb * groups + g;
+    const float4 *p = part + ((size_t)n * groups + g) * sb;
     Welford acc = {0.0f, 0.0f, 0.0f};
     int b = tid;
     // eight independent loads in flight per thread
     for (; b + 7 * kFinalThreads < sb; b += 8 * kFinalThreads) {
         float4 e[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) e[u] = p[(size_t)(b + u * kFinalThreads) * groups];
+        for (int u = 0; u < 8; ++u) e[u] = p[b + u * kFinalThreads];
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc = chan_merge(acc, Welford{e[u].x, e[u].y, e[u].z});
     }
     for (; b < sb; b += kFinalThreads) {
-        const float4 e = p[(size_t)b * groups];
+        const float4 e = p[b];
         acc = chan_merge(acc, Welford{e.x, e.y, e.z});
     }
 #pragma unroll
@@ -250,34 +252,40 @@ __global__ __launch_bounds__(kMaxThreads) void gn_apply_kernel(const _Float16 *_
     const half8_t *xs = reinterpret_cast<const half8_t *>(x + (size_t)n * thw * c);
     half8_t *ys = reinterpret_cast<half8_t *>(y + (size_t)n * thw * c);
     int64_t v = (int64_t)blockIdx.x * (blockDim.x / vpv) + tid / vpv;
-    // four 16-byte loads in flight per thread
-    for (; v + 3 * vox_step < thw; v += 4 * vox_step) {
-        half8_t h[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) h[u] = __builtin_nontemporal_load(xs + (v + u * vox_step) * vpv + vi);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            half8_t o;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                float t = fmaf((float)h[u][q], a[q], bsh[q]);
-                if (SILU) t = silu_f32(t);
-                o[q] = (_Float16)t;
-            }
-            __builtin_nontemporal_store(o, ys + (v + u * vox_step) * vpv + vi);
-        }
-    }
-    for (; v < thw; v += vox_step) {
-        const half8_t h0 = __builtin_nontemporal_load(xs + v * vpv + vi);
-        half8_t o0;
+    auto apply = [&](const half8_t h) {
+        half8_t o;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            float t0 = fmaf((float)h0[q], a[q], bsh[q]);
-            if (SILU) t0 = silu_f32(t0);
-            o0[q] = (_Float16)t0;
+            float t = fmaf((float)h[q], a[q], bsh[q]);
+            if (SILU) t = silu_f32(t);
+            o[q] = (_Float16)t;
         }
-        __builtin_nontemporal_store(o0, ys + v * vpv + vi);
+        return o;
+    };
+    // four 16-byte loads per batch; the next batch is in flight while this
+    // one is converted and stored
+    constexpr int U = 4;
+    half8_t h[U];
+    if (v + (U - 1) * vox_step < thw) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) h[u] = __builtin_nontemporal_load(xs + (v + u * vox_step) * vpv + vi);
+        for (;;) {
+            const int64_t vn = v + U * vox_step;
+            const bool more = vn + (U - 1) * vox_step < thw;
+            half8_t hn[U];
+            if (more) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) hn[u] = __builtin_nontemporal_load(xs + (vn + u * vox_step) * vpv + vi);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) __builtin_nontemporal_store(apply(h[u]), ys + (v + u * vox_step) * vpv + vi);
+            v = vn;
+            if (!more) break;
+#pragma unroll
+            for (int u = 0; u < U; ++u) h[u] = hn[u];
+        }
     }
+    for (; v < thw; v += vox_step) __builtin_nontemporal_store(apply(__builtin_nontemporal_load(xs + v * vpv + vi)), ys + v * vpv + vi);
 }
 
 }  // namespace
@@ -295,7 +303,7 @@ hipError_t launch_groupnorm_silu(const _Float16 *x, const _Float16 *gamma, const
     float *scale = reinterpret_cast<float *>(base);
     float *shift = scale + (size_t)n * c;
     float4 *part = reinterpret_cast<float4 *>(base + off_part(n, c));
-    hipLaunchKernelGGL(gn_stats_kernel, dim3(g.sb, n), dim3(g.threads), 0, s, x, thw, c, groups, g.sb, part);
+    hipLaunchKernelGGL(gn_stats_kernel, dim3(g.sb, n), dim3(g.sthreads), 0, s, x, thw, c, groups, g.sb, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gn_final_kernel, dim3(groups, n), dim3(kFinalThreads), 0, s, part, g.sb, c, groups, eps,
@@ -303,10 +311,10 @@ hipError_t launch_groupnorm_silu(const _Float16 *x, const _Float16 *gamma, const
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (silu)
-        hipLaunchKernelGGL(gn_apply_kernel<true>, dim3(g.ab, n), dim3(g.threads), 0, s, x, y, thw, c, scale,
+        hipLaunchKernelGGL(gn_apply_kernel<true>, dim3(g.ab, n), dim3(g.athreads), 0, s, x, y, thw, c, scale,
                            shift);
     else
-        hipLaunchKernelGGL(gn_apply_kernel<false>, dim3(g.ab, n), dim3(g.threads), 0, s, x, y, thw, c, scale,
+        hipLaunchKernelGGL(gn_apply_kernel<false>, dim3(g.ab, n), dim3(g.athreads), 0, s, x, y, thw, c, scale,
                            shift);
     return hipGetLastError();
 }

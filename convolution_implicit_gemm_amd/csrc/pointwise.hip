@@ -5,8 +5,10 @@
 // channels the arithmetic intensity is ~85 flop/byte, far below the MI355X
 // ridge, so the kernel is designed around moving bytes:
 //  * persistent blocks (two or more per CU), each streaming 64-row tiles of
-//    input through a double-buffered, bank-swizzled LDS ring with
-//    buffer_load ... lds (no VGPR staging);
+//    input through a bank-swizzled LDS ring of 64 KB (two tiles at 256
+//    channels) with buffer_load ... lds (no VGPR staging); measured, two
+//    blocks per CU with this ring beat deeper rings with fewer blocks and
+//    shorter tiles with more;
 //  * each wave keeps its 32 output channels x all Cin of weights in VGPRs as
 //    MFMA A-fragments, loaded once per block;
 //  * every tile gets its own buffer resource spanning exactly its valid rows,
@@ -14,9 +16,8 @@
 //  * fp16 MFMA 32x32x16 with fp32 accumulation; bias / residual added in fp32,
 //    one RNE rounding; the rounded tile is staged in LDS so that every store
 //    is a 16-byte piece of a whole output row.
-// Each K-iteration ends with s_waitcnt vmcnt(0): loads and stores share one
-// counter on gfx9, so the kernel never relies on their relative completion
-// order; the second block per CU keeps memory busy meanwhile.
+// Loads and stores share one counter on gfx9; the per-tile wait counts only
+// the loads issued after the tile's own, which loads retire in order.
 #include "c3d_internal.h"
 
 namespace c3d {
@@ -56,7 +57,16 @@ __device__ __forceinline__ void pw_dma16(pw_rsrc r, char *lds, uint32_t voff) {
 #endif
 }
 
-__device__ __forceinline__ void pw_wait_all_and_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Wait until at most N vector-memory operations of this wave are in flight and
+// its LDS traffic is done, then meet the other waves.  Loads retire in issue
+// order among themselves, so "at most N" with N counting only the loads issued
+// after a tile's loads guarantees that tile has landed, whatever the order in
+// which the stores in between complete.
+template <int N>
+__device__ __forceinline__ void pw_wait_and_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 // 16-byte chunk swizzle within a row of CPR chunks: 32 consecutive rows read at
 // one logical chunk land on distinct banks in every 8- and 16-lane group.
@@ -71,19 +81,29 @@ __device__ __forceinline__ int pw_swz(int row) {
 constexpr int kPwRows = 64;   // voxels per tile
 constexpr int kPwWaves = 4;   // 4 x 32 output channels per block
 
+// Input ring depth: about 64 KB of tiles per block, at most 8.
+template <int CIN>
+constexpr int pw_ring() {
+    constexpr int tile = kPwRows * CIN * 2;
+    constexpr int nb = 64 * 1024 / tile;
+    return nb > 8 ? 8 : (nb < 2 ? 2 : nb);
+}
+
 template <int CIN>
 __global__ __launch_bounds__(256, 2) void pointwise_kernel(PwParams p) {
     constexpr int RB = CIN * 2;                 // bytes per input row
     constexpr int CPR = CIN / 8;                // 16-byte chunks per row
     constexpr int BM = kPwRows;                 // rows per tile
+    constexpr int NB = pw_ring<CIN>();          // ring depth
     constexpr int TILE_BYTES = BM * RB;
     constexpr int RPI = 1024 / RB;              // rows per 1 KiB load instruction
     constexpr int NI = TILE_BYTES / 1024 / kPwWaves;  // load instructions per wave per tile
     constexpr int KF = CIN / 16;                // MFMA k-steps
     constexpr int SUB = BM / 32;                // 32-voxel sub-tiles per tile
+    static_assert(BM % 32 == 0, "tiles of whole 32-voxel sub-tiles");
     static_assert(RB <= 1024 && 1024 % RB == 0 && NI >= 1, "CIN in {64, 128, 256, 512}");
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[NB * TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char obuf[kPwWaves * BM * 64];  // output staging
 
     const int lane = threadIdx.x & 63;
@@ -115,60 +135,72 @@ __global__ __launch_bounds__(256, 2) void pointwise_kernel(PwParams p) {
 #pragma unroll
     for (int f = 0; f < KF; ++f) koff[f] = rrow * RB + (((2 * f + rhi) ^ pw_swz<CPR>(rrow)) * 16);
 
+    // bias of this lane's 16 output channels, once: loads inside the loop would
+    // sit between the prefetched tiles in issue order and lengthen every wait
+    float bv[4][4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        pw_half4 b4 = {};
+        if (p.bias && live) b4 = *reinterpret_cast<const pw_half4 *>(p.bias + co0 + 8 * g + 4 * rhi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[g][e] = (float)b4[e];
+    }
+
     const int M = (int)p.M;
     const int ntiles = (M + BM - 1) / BM;
+    // Tiles past the end are fetched as empty ranges (every lane reads zeros),
+    // so every wave issues the same number of loads per tile.
     auto issue = [&](int tile, int buf) {
         const int m0 = tile * BM;
-        const int rows = M - m0 < BM ? M - m0 : BM;
-        const pw_rsrc r = pw_make_rsrc(p.x + (int64_t)m0 * CIN, (uint32_t)(rows * RB));
+        const int rows = tile < ntiles ? (M - m0 < BM ? M - m0 : BM) : 0;
+        const pw_rsrc r = pw_make_rsrc(p.x + (int64_t)(tile < ntiles ? m0 : 0) * CIN, (uint32_t)(rows * RB));
         char *sb = smem + buf * TILE_BYTES;
 #pragma unroll
         for (int j = 0; j < NI; ++j) pw_dma16(r, sb + (j * kPwWaves + wv) * 1024, voff[j]);
     };
 
+    const int step = (int)gridDim.x;
     int tile = blockIdx.x;
-    if (tile < ntiles) issue(tile, 0);
-    for (int it = 0; tile < ntiles; ++it, tile += gridDim.x) {
-        pw_wait_all_and_barrier();  // this tile landed; everyone is done with the other buffer
-        const int next = tile + (int)gridDim.x;
-        if (next < ntiles) issue(next, (it + 1) & 1);
+    // prologue: tiles 0..NB-2 of this block
+#pragma unroll
+    for (int k = 0; k < NB - 1; ++k) issue(tile + k * step, k);
+    int buf = 0;
+    for (; tile < ntiles; tile += step) {
+        // this tile landed; everyone is done with the buffer refilled next
+        pw_wait_and_barrier<(NB - 2) * NI>();
+        issue(tile + (NB - 1) * step, buf == 0 ? NB - 1 : buf - 1);
+        const char *sb = smem + buf * TILE_BYTES;
+        buf = buf + 1 == NB ? 0 : buf + 1;
         if (!live) continue;
-        const char *sb = smem + (it & 1) * TILE_BYTES;
         pw_f32x16 acc[SUB];
 #pragma unroll
-        for (int s = 0; s < SUB; ++s)
+        for (int u = 0; u < SUB; ++u)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[s][e] = 0.0f;
+            for (int e = 0; e < 16; ++e) acc[u][e] = 0.0f;
 #pragma unroll
         for (int f = 0; f < KF; ++f) {
 #pragma unroll
-            for (int s = 0; s < SUB; ++s) {
-                const pw_half8 b = *reinterpret_cast<const pw_half8 *>(sb + s * 32 * RB + koff[f]);
-                acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[f], b, acc[s], 0, 0, 0);
+            for (int u = 0; u < SUB; ++u) {
+                const pw_half8 b = *reinterpret_cast<const pw_half8 *>(sb + u * 32 * RB + koff[f]);
+                acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[f], b, acc[u], 0, 0, 0);
             }
         }
         // epilogue: + bias (+ residual) in fp32 and one RNE rounding in registers,
         // then through LDS so that the block writes whole output rows with
         // 16-byte stores (scattered 8-byte stores of 256-byte rows waste most of
         // each memory transaction).  Lane holds channels co0 + 8g + 4*(lane/32) + e
-        // of voxel lane%32.
+        // of voxel 32u + lane%32.
         const int m0 = tile * BM;
         char *ob = obuf + wv * (BM * 64);  // this wave's [BM voxels][32 ch] fp16, row-swizzled
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int co = co0 + 8 * g + 4 * rhi;
-            float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (p.bias) {
-                const pw_half4 b4 = *reinterpret_cast<const pw_half4 *>(p.bias + co);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) bv[e] = (float)b4[e];
-            }
-#pragma unroll
-            for (int s = 0; s < SUB; ++s) {
-                const int vrow = s * 32 + rrow;
+            for (int u = 0; u < SUB; ++u) {
+                const int vrow = u * 32 + rrow;
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[s][4 * g + e] + bv[e];
+                for (int e = 0; e < 4; ++e) v[e] = acc[u][4 * g + e] + bv[g][e];
                 if (p.res && m0 + vrow < M) {
                     const pw_half4 r4 = *reinterpret_cast<const pw_half4 *>(p.res + (int64_t)(m0 + vrow) * p.Cout + co);
 #pragma unroll
@@ -200,19 +232,29 @@ __global__ __launch_bounds__(256, 2) void pointwise_kernel(PwParams p) {
             }
         }
     }
-    pw_wait_all_and_barrier();
+    pw_wait_and_barrier<0>();  // drain the prefetches past the end before LDS is released
+}
+
+template <int CIN>
+PwGeom pw_geom(int32_t cout, int64_t m) {
+    // as many resident blocks as LDS allows, up to four per CU
+    constexpr int lds = pw_ring<CIN>() * kPwRows * CIN * 2 + kPwWaves * kPwRows * 64;
+    constexpr int per_cu = (160 * 1024 / lds) < 4 ? (160 * 1024 / lds) : 4;
+    const int64_t ntiles = (m + kPwRows - 1) / kPwRows;
+    const int64_t cap = 256 * per_cu;
+    PwGeom g;
+    g.rows = kPwRows;
+    g.ring = pw_ring<CIN>();
+    g.grid_x = ntiles < cap ? ntiles : cap;
+    g.grid_y = (cout + 32 * kPwWaves - 1) / (32 * kPwWaves);
+    return g;
 }
 
 template <int CIN>
 hipError_t launch_pw(const PwParams &p, hipStream_t s) {
-    // as many resident blocks as LDS allows, up to four per CU
-    constexpr int lds = 2 * kPwRows * CIN * 2 + kPwWaves * kPwRows * 64;
-    constexpr int per_cu = (160 * 1024 / lds) < 4 ? (160 * 1024 / lds) : 4;
-    const int64_t ntiles = (p.M + kPwRows - 1) / kPwRows;
-    const int64_t cap = 256 * per_cu;
-    const int64_t blocks = ntiles < cap ? ntiles : cap;
-    const unsigned gy = (unsigned)((p.Cout + 32 * kPwWaves - 1) / (32 * kPwWaves));
-    hipLaunchKernelGGL(pointwise_kernel<CIN>, dim3((unsigned)blocks, gy), dim3(64 * kPwWaves), 0, s, p);
+    const PwGeom g = pw_geom<CIN>(p.Cout, p.M);
+    hipLaunchKernelGGL(pointwise_kernel<CIN>, dim3((unsigned)g.grid_x, (unsigned)g.grid_y), dim3(64 * kPwWaves), 0, s,
+                       p);
     return hipGetLastError();
 }
 
@@ -220,6 +262,15 @@ hipError_t launch_pw(const PwParams &p, hipStream_t s) {
 
 bool pointwise_supported(int32_t cin, int32_t cout) {
     return (cin == 64 || cin == 128 || cin == 256 || cin == 512) && cout % 32 == 0;
+}
+
+PwGeom pointwise_geometry(int32_t cin, int32_t cout, int64_t m) {
+    switch (cin) {
+        case 64: return pw_geom<64>(cout, m);
+        case 128: return pw_geom<128>(cout, m);
+        case 256: return pw_geom<256>(cout, m);
+        default: return pw_geom<512>(cout, m);
+    }
 }
 
 hipError_t launch_pointwise(const PwParams &p, hipStream_t s) {
