@@ -10,6 +10,10 @@ decoder-block time in ms (GN+SiLU, causal conv, GN+SiLU, causal conv + x;
 N=1, C=256, T=17, 128x128), and per-kernel figures of the other hot-path
 kernels under "kernels".
 
+It ends with the machine's own ceilings (conv3d_calibrate_mfma / _hbm: dense
+fp16 MFMA on random operands with the shader clock, HBM read and copy), and
+each roofline figure is also given as a fraction of those.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-seconds S]
 """
 from __future__ import annotations
@@ -123,7 +127,19 @@ def cpu_baseline_leg(d, y_dev, info, target_s, np):
             "sample": "%d output voxels x all %d channels (%.3g GFLOP of %.3g), fp64 "
                       "seven-loop oracle, %.1f s wall" % (nvox, s.cout, flops / 1e9,
                                                           info.flops / 1e9, dt),
-            "seconds": dt, "gpu_matches_oracle_on_sample": ok}
+            "seconds": dt, "gpu_matches_oracle_on_sample": ok,
+            "host_cpu": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -135,6 +151,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall seconds of oracle work for cpu_baseline (0 disables it)")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel extras")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the MFMA / HBM ceiling measurements at the end")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with one 1 GiB device-to-device copy (scales byte counters in profiles)")
     args = ap.parse_args()
@@ -172,6 +190,7 @@ def main():
     log("timing %d steps after %d warmup" % (args.steps, args.warmup))
     ms, per = time_steps(step, args.steps, args.warmup, torch)
     kernel_ms = sum(per) / len(per)
+    per_sorted = sorted(per)
     value = info.flops / (ms * 1e-3) / 1e12
     achieved = info.flops / (kernel_ms * 1e-3) / 1e12
     kname = info.kernel_name.decode()
@@ -198,6 +217,10 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
                      "traffic": committed_traffic(kname, src_hash),
                      "kernel_ms": round(kernel_ms, 4), "source_sha256_16": src_hash},
+        "timing": {"launch_ms_mean": round(kernel_ms, 4),
+                   "launch_ms_median": round(per_sorted[len(per) // 2], 4),
+                   "launch_ms_min": round(per_sorted[0], 4), "launches": len(per),
+                   "clock": "HIP events on the launch stream, one pair per step"},
     }
 
     # ---- decoder block: GN+SiLU -> causal conv -> GN+SiLU -> causal conv + x
@@ -222,6 +245,24 @@ def main():
 
     bms, bper = time_steps(block, max(5, args.steps // 2), max(2, args.warmup), torch)
     result["decoder_block_ms"] = round(sum(bper) / len(bper), 4)
+    # per-launch breakdown: events between the four calls, averaged over 20 blocks
+    stream = torch.cuda.current_stream()
+    parts = {"gn1": [], "conv1": [], "gn2": [], "conv2_plus_x": []}
+    for _ in range(20):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        ev[0].record(stream)
+        c3d.groupnorm_silu(bx, bt["gamma1"], bt["beta1"], a1, 1, thw, s4.cin, 32, 1e-6, True, gws)
+        ev[1].record(stream)
+        c3d.conv3d_forward(bp1, a1, bt["w1"], bt["b1"], None, c1, bws1)
+        ev[2].record(stream)
+        c3d.groupnorm_silu(c1, bt["gamma2"], bt["beta2"], a2, 1, thw, s4.cout, 32, 1e-6, True, gws)
+        ev[3].record(stream)
+        c3d.conv3d_forward(bp2, a2, bt["w2"], bt["b2"], bx, out, bws2)
+        ev[4].record(stream)
+        torch.cuda.synchronize()
+        for k, name in enumerate(parts):
+            parts[name].append(ev[k].elapsed_time(ev[k + 1]))
+    result["decoder_block_breakdown_ms"] = {k: round(sum(v) / len(v), 4) for k, v in parts.items()}
     result["decoder_block_config"] = ("GN(32, eps 1e-6)+SiLU -> causal conv3d 3x3x3 -> GN+SiLU -> "
                                       "causal conv3d 3x3x3 -> +x; N=1 C=256 T=17 H=W=128 fp16")
 
@@ -236,15 +277,25 @@ def main():
         kern["causal_conv_256_T17"] = {"ms": round(t, 4), "TFLOP/s": round(conv_flops / t / 1e9, 1),
                                        "kernel": bp1.info().kernel_name.decode()}
 
+        # three input copies in rotation (428 MB > the 256 MB MALL), so no call
+        # finds its input already cached by the previous one
+        gx = [bx, bx.clone(), bx.clone()]
+        gi = [0]
+
         def gn_only():
-            c3d.groupnorm_silu(bx, bt["gamma1"], bt["beta1"], a1, 1, thw, s4.cin, 32, 1e-6, True,
-                               gws)
-        _, p = time_steps(gn_only, 10, 2, torch)
-        t = sum(p) / len(p)
+            c3d.groupnorm_silu(gx[gi[0] % 3], bt["gamma1"], bt["beta1"], a1, 1, thw, s4.cin, 32,
+                               1e-6, True, gws)
+            gi[0] += 1
+        _, p = time_steps(gn_only, 30, 6, torch)
+        p = sorted(p)
+        t = p[len(p) // 2]
         sbytes = bx.numel() * 2
-        kern["groupnorm_silu_256_T17"] = {"ms": round(t, 4),
+        kern["groupnorm_silu_256_T17"] = {"ms_median": round(t, 4), "ms_min": round(p[0], 4),
                                           "GB/s_effective_2S": round(2 * sbytes / t / 1e6, 1),
-                                          "GB/s_as_implemented_3S": round(3 * sbytes / t / 1e6, 1)}
+                                          "GB/s_as_implemented_3S": round(3 * sbytes / t / 1e6, 1),
+                                          "frac_of_hbm_3S": round(3 * sbytes / t / 1e6 / PEAK_HBM_GBS, 3),
+                                          "inputs": "3 copies in rotation"}
+        del gx
 
         s1f = workloads.CAUSAL_256_T1
         pt1 = c3d.conv3d_plan(desc_of(c3d, s1f, c3d.CONV3D_F_BIAS))
@@ -300,6 +351,31 @@ def main():
         result["cpu_baseline"] = cpu_baseline_leg(d1, y.cpu().numpy(), info, args.cpu_seconds, np)
     else:
         result["cpu_baseline"] = None
+
+    if not args.no_calibration:
+        log("machine ceilings: MFMA on random operands, HBM read and copy")
+        scratch = torch.empty(c3d.conv3d_calibrate_scratch_bytes(), dtype=torch.uint8, device=dev)
+        mfma_tf, sclk = c3d.conv3d_calibrate_mfma(scratch)
+        del scratch
+        nb = 2 << 30
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        rd, cp = c3d.conv3d_calibrate_hbm(src, dst, nb)
+        del src, dst
+        result["calibration"] = {"mfma_fp16_tflops_random_operands": round(mfma_tf, 1),
+                                 "sclk_mhz_during_mfma": round(sclk, 0),
+                                 "hbm_read_gbs": round(rd, 1), "hbm_copy_gbs_read_plus_write": round(cp, 1)}
+        rf = result["roofline"]
+        rf["frac_of_measured"] = round(rf["achieved"] / mfma_tf, 4)
+        if "kernels" in result:
+            k = result["kernels"]
+            if "pointwise_256to128_T33_256x256" in k:
+                k["pointwise_256to128_T33_256x256"]["frac_of_measured_copy"] = round(
+                    k["pointwise_256to128_T33_256x256"]["GB/s"] / cp, 3)
+            if "groupnorm_silu_256_T17" in k:
+                k["groupnorm_silu_256_T17"]["frac_of_measured_copy_3S"] = round(
+                    k["groupnorm_silu_256_T17"]["GB/s_as_implemented_3S"] / cp, 3)
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

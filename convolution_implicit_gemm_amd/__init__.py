@@ -34,7 +34,8 @@ CONV3D_PATH_T1_FOLD = 1
 CONV3D_PATH_POINTWISE = 2
 
 EXPORTED = ("conv3d_plan", "conv3d_plan_query", "conv3d_plan_destroy", "conv3d_forward",
-            "groupnorm_silu_workspace", "groupnorm_silu", "conv3d_status_str",
+            "groupnorm_silu_workspace", "groupnorm_silu", "conv3d_calibrate_scratch_bytes",
+            "conv3d_calibrate_mfma", "conv3d_calibrate_hbm", "conv3d_status_str",
             "conv3d_last_error", "conv3d_version")
 
 
@@ -97,6 +98,13 @@ def load_library(path: str = LIB_PATH):
     lib.conv3d_last_error.restype = ctypes.c_char_p
     lib.conv3d_version.argtypes = []
     lib.conv3d_version.restype = i32
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.conv3d_calibrate_scratch_bytes.argtypes = []
+    lib.conv3d_calibrate_scratch_bytes.restype = sz
+    lib.conv3d_calibrate_mfma.argtypes = [vp, sz, dp, dp, vp]
+    lib.conv3d_calibrate_mfma.restype = ctypes.c_int
+    lib.conv3d_calibrate_hbm.argtypes = [vp, vp, sz, dp, dp, vp]
+    lib.conv3d_calibrate_hbm.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -193,6 +201,28 @@ def groupnorm_silu(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, worksp
     _check(load_library().groupnorm_silu(_addr(x), _addr(gamma), _addr(beta), _addr(y), n, thw, c,
                                          groups, float(eps), 1 if apply_silu else 0,
                                          _addr(workspace), workspace_bytes, _stream(stream)))
+
+
+def conv3d_calibrate_scratch_bytes() -> int:
+    return load_library().conv3d_calibrate_scratch_bytes()
+
+
+def conv3d_calibrate_mfma(scratch, scratch_bytes=None, stream=None):
+    """(TFLOP/s, shader MHz) of dense fp16 MFMA chains on random operands; synchronises."""
+    if scratch_bytes is None:
+        scratch_bytes = scratch.numel() * scratch.element_size()
+    tf, mhz = ctypes.c_double(), ctypes.c_double()
+    _check(load_library().conv3d_calibrate_mfma(_addr(scratch), scratch_bytes, ctypes.byref(tf),
+                                                ctypes.byref(mhz), _stream(stream)))
+    return tf.value, mhz.value
+
+
+def conv3d_calibrate_hbm(src, dst, nbytes, stream=None):
+    """(read GB/s, copy GB/s, read + write counted) of 16-byte streams; synchronises."""
+    rd, cp = ctypes.c_double(), ctypes.c_double()
+    _check(load_library().conv3d_calibrate_hbm(_addr(src), _addr(dst), nbytes, ctypes.byref(rd),
+                                               ctypes.byref(cp), _stream(stream)))
+    return rd.value, cp.value
 
 
 def conv3d_status_str(status: int) -> str:

@@ -417,3 +417,33 @@ conv3d_status groupnorm_silu(const void *x, const void *gamma, const void *beta,
 }
 
 }  // extern "C"
+
+size_t conv3d_calibrate_scratch_bytes(void) { return c3d::calibrate_scratch_bytes(); }
+
+conv3d_status conv3d_calibrate_mfma(void *scratch, size_t scratch_bytes, double *tflops, double *sclk_mhz,
+                                    void *stream) {
+    if (!tflops || !sclk_mhz) return fail(CONV3D_ERR_INVALID_ARG, "tflops and sclk_mhz are required");
+    if (!scratch || misaligned(scratch)) return fail(CONV3D_ERR_INVALID_ARG, "scratch must be 16-byte aligned");
+    if (scratch_bytes < c3d::calibrate_scratch_bytes())
+        return fail(CONV3D_ERR_WORKSPACE, "scratch of %zu bytes needed, %zu given", c3d::calibrate_scratch_bytes(),
+                    scratch_bytes);
+    conv3d_status st = check_device();
+    if (st != CONV3D_OK) return st;
+    hipError_t e = c3d::calibrate_mfma(scratch, static_cast<hipStream_t>(stream), tflops, sclk_mhz);
+    if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "mfma calibration: %s", hipGetErrorString(e));
+    return ok();
+}
+
+conv3d_status conv3d_calibrate_hbm(const void *src, void *dst, size_t bytes, double *read_gbs, double *copy_gbs,
+                                   void *stream) {
+    if (!src || !dst || !read_gbs || !copy_gbs)
+        return fail(CONV3D_ERR_INVALID_ARG, "src, dst, read_gbs and copy_gbs are required");
+    if (misaligned(src) || misaligned(dst) || bytes % 16 || bytes < 16)
+        return fail(CONV3D_ERR_INVALID_ARG, "16-byte aligned buffers and a positive multiple of 16 bytes needed");
+    if (overlap(src, bytes, dst, bytes)) return fail(CONV3D_ERR_INVALID_ARG, "src and dst overlap");
+    conv3d_status st = check_device();
+    if (st != CONV3D_OK) return st;
+    hipError_t e = c3d::calibrate_hbm(src, dst, bytes, static_cast<hipStream_t>(stream), read_gbs, copy_gbs);
+    if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "hbm calibration: %s", hipGetErrorString(e));
+    return ok();
+}

@@ -85,4 +85,10 @@ hipError_t launch_groupnorm_silu(const _Float16 *x, const _Float16 *gamma, const
                                  _Float16 *y, int32_t n, int64_t thw, int32_t c, int32_t groups,
                                  float eps, int32_t silu, void *ws, hipStream_t s);
 
+// Measurement aids (calibrate.hip): machine ceilings for the kernels above.
+size_t calibrate_scratch_bytes();
+hipError_t calibrate_mfma(void *scratch, hipStream_t s, double *tflops, double *sclk_mhz);
+hipError_t calibrate_hbm(const void *src, void *dst, size_t bytes, hipStream_t s, double *read_gbs,
+                         double *copy_gbs);
+
 }  // namespace c3d

@@ -1,0 +1,205 @@
+// Measurement aids: the MFMA and HBM ceilings of the machine the library runs
+// on, against which the conv (MFMA-bound) and the 1x1x1 / GroupNorm kernels
+// (HBM-bound) are judged next to the published peaks.  Not on the conv path.
+//
+//  * MFMA: every CU runs independent v_mfma_f32_32x32x16_f16 chains, 8 waves
+//    per CU, on fp16 operands from a fixed pseudo-random pattern, rotated
+//    every instruction.  Operand entropy matters on this chip: power limits
+//    the clock, so constant or low-entropy data runs faster than real
+//    activations and weights.  The shader clock is measured in the kernel as
+//    the ratio of the shader-clock counter (s_memtime) to the 100 MHz
+//    reference counter (s_memrealtime).
+//  * HBM: a read-only stream and a copy (read + write), 16-byte non-temporal
+//    accesses, many loads in flight per thread.
+#include <hip/hip_runtime.h>
+
+#include "conv3d.h"
+#include "c3d_internal.h"
+
+namespace c3d {
+namespace {
+
+typedef _Float16 cal_half8 __attribute__((ext_vector_type(8)));
+typedef float cal_f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t cal_u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCalFrags = 1024;  // 16-byte fragments of the operand pattern
+constexpr int kCalBlocks = 512, kCalThreads = 256;
+// scratch layout: operand pattern, then per-block clock samples, then sink
+constexpr size_t kCalPatternBytes = (size_t)kCalFrags * 64 * 16;
+constexpr size_t kCalClockBytes = (size_t)kCalBlocks * 2 * sizeof(uint64_t);
+constexpr size_t kCalScratch = kCalPatternBytes + kCalClockBytes + 256;
+
+__global__ __launch_bounds__(256) void cal_fill_kernel(uint32_t *p, int64_t words) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= words) return;
+    // two fp16 values in (-1, 1) per word from an integer hash of the index
+    uint32_t h = (uint32_t)i * 2654435761u;
+    h ^= h >> 15;
+    h *= 2246822519u;
+    h ^= h >> 13;
+    const _Float16 a = (_Float16)((float)(h & 0xFFFF) / 32768.0f - 1.0f);
+    const _Float16 b = (_Float16)((float)(h >> 16) / 32768.0f - 1.0f);
+    p[i] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__global__ __launch_bounds__(kCalThreads) void cal_mfma_kernel(const cal_half8 *pat, uint64_t *clocks, float *sink,
+                                                               int iters) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int base = (blockIdx.x * 4 + wv) * 16;
+    cal_half8 a[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = pat[((base + i) % kCalFrags) * 64 + lane];
+        b[i] = pat[((base + 8 + i) % kCalFrags) * 64 + lane];
+    }
+    cal_f32x16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+    uint64_t c0 = 0, r0 = 0;
+    if (threadIdx.x == 0) {
+        c0 = __builtin_amdgcn_s_memtime();
+        r0 = __builtin_amdgcn_s_memrealtime();
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[(k + i) & 7], b[(k + 3 * i) & 7], acc[i], 0, 0, 0);
+    }
+    if (threadIdx.x == 0) {
+        const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+        clocks[2 * blockIdx.x] = c1 - c0;
+        clocks[2 * blockIdx.x + 1] = r1 - r0;
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[i][e];
+    if (s == 1.2345e30f) sink[0] = s;  // keeps the chains live; never true
+}
+
+template <int U>
+__global__ __launch_bounds__(256) void cal_read_kernel(const cal_u32x4 *__restrict__ a, int64_t n, uint32_t *sink) {
+    cal_u32x4 acc = {0, 0, 0, 0};
+    const int64_t stride = (int64_t)gridDim.x * 256 * U;
+    for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n; base += stride) {
+        cal_u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + (int64_t)u * 256;
+            v[u] = i < n ? __builtin_nontemporal_load(a + i) : cal_u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u];
+    }
+    if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9e3779b9u && threadIdx.x == 0) sink[0] = acc[0];
+}
+
+template <int U>
+__global__ __launch_bounds__(256) void cal_copy_kernel(const cal_u32x4 *__restrict__ a, cal_u32x4 *__restrict__ b,
+                                                       int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * 256 * U;
+    for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n; base += stride) {
+        cal_u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + (int64_t)u * 256;
+            if (i < n) v[u] = __builtin_nontemporal_load(a + i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + (int64_t)u * 256;
+            if (i < n) __builtin_nontemporal_store(v[u], b + i);
+        }
+    }
+}
+
+// Mean event time (ms) of `reps` launches after one untimed launch.
+template <typename F>
+hipError_t time_launches(F launch, int reps, hipStream_t s, float *ms) {
+    hipEvent_t e0, e1;
+    hipError_t e = hipEventCreate(&e0);
+    if (e != hipSuccess) return e;
+    e = hipEventCreate(&e1);
+    if (e != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return e;
+    }
+    launch();
+    e = hipEventRecord(e0, s);
+    for (int r = 0; r < reps && e == hipSuccess; ++r) {
+        launch();
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(ms, e0, e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    *ms /= (float)reps;
+    return e;
+}
+
+}  // namespace
+
+size_t calibrate_scratch_bytes() { return kCalScratch; }
+
+hipError_t calibrate_mfma(void *scratch, hipStream_t s, double *tflops, double *sclk_mhz) {
+    char *base = static_cast<char *>(scratch);
+    uint32_t *pat = reinterpret_cast<uint32_t *>(base);
+    uint64_t *clocks = reinterpret_cast<uint64_t *>(base + kCalPatternBytes);
+    float *sink = reinterpret_cast<float *>(base + kCalPatternBytes + kCalClockBytes);
+    const int64_t words = (int64_t)(kCalPatternBytes / 4);
+    hipLaunchKernelGGL(cal_fill_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, pat, words);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int iters = 4000;
+    float ms = 0.0f;
+    e = time_launches(
+        [&] {
+            hipLaunchKernelGGL(cal_mfma_kernel, dim3(kCalBlocks), dim3(kCalThreads), 0, s,
+                               reinterpret_cast<const cal_half8 *>(pat), clocks, sink, iters);
+        },
+        3, s, &ms);
+    if (e != hipSuccess) return e;
+    const double flops = (double)kCalBlocks * (kCalThreads / 64) * iters * 64 * 32768.0;
+    *tflops = flops / (ms * 1e-3) / 1e12;
+    uint64_t host[2 * kCalBlocks];
+    e = hipMemcpyAsync(host, clocks, sizeof(host), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return e;
+    double clk = 0.0, ref = 0.0;
+    for (int b = 0; b < kCalBlocks; ++b) {
+        clk += (double)host[2 * b];
+        ref += (double)host[2 * b + 1];
+    }
+    *sclk_mhz = ref > 0.0 ? 100.0 * clk / ref : 0.0;
+    return hipSuccess;
+}
+
+hipError_t calibrate_hbm(const void *src, void *dst, size_t bytes, hipStream_t s, double *read_gbs, double *copy_gbs) {
+    const int64_t n = (int64_t)(bytes / 16);
+    const cal_u32x4 *a = static_cast<const cal_u32x4 *>(src);
+    cal_u32x4 *b = static_cast<cal_u32x4 *>(dst);
+    float ms = 0.0f;
+    hipError_t e = time_launches(
+        [&] {
+            hipLaunchKernelGGL(cal_read_kernel<4>, dim3(8192), dim3(256), 0, s, a, n,
+                               reinterpret_cast<uint32_t *>(b));
+        },
+        5, s, &ms);
+    if (e != hipSuccess) return e;
+    *read_gbs = (double)n * 16 / (ms * 1e-3) / 1e9;
+    e = time_launches([&] { hipLaunchKernelGGL(cal_copy_kernel<4>, dim3(8192), dim3(256), 0, s, a, b, n); }, 5, s,
+                      &ms);
+    if (e != hipSuccess) return e;
+    *copy_gbs = 2.0 * (double)n * 16 / (ms * 1e-3) / 1e9;
+    return hipSuccess;
+}
+
+}  // namespace c3d

@@ -15,10 +15,11 @@
  * item 4286, paragraph on MPS tweaks and the fused kernel).
  *
  * Conventions shared by every entry point:
- *  - No entry point aborts, throws or synchronises the device.  Work is
- *    enqueued on the caller's stream (a hipStream_t passed as void*; NULL is
- *    the default stream), after the A1111 Metal fork's lesson that a native
- *    op must go into the framework's current stream without its own commit.
+ *  - No entry point aborts or throws, and none but the two measurement aids
+ *    at the end synchronises the device.  Work is enqueued on the caller's
+ *    stream (a hipStream_t passed as void*; NULL is the default stream), after
+ *    the A1111 Metal fork's lesson that a native op must go into the
+ *    framework's current stream without its own commit.
  *  - The caller owns every device buffer.  The library never allocates
  *    device memory.  Device pointers must be 16-byte aligned.
  *  - All tensors are fp16 (IEEE binary16) unless stated; accumulation is fp32.
@@ -166,6 +167,31 @@ conv3d_status groupnorm_silu(const void *x, const void *gamma, const void *beta,
                              int32_t n, int64_t thw, int32_t c, int32_t groups, float eps,
                              int32_t apply_silu, void *workspace, size_t workspace_bytes,
                              void *stream);
+
+/*
+ * Measurement aids, not on the convolution path: the ceilings of the machine
+ * the library runs on, to report the kernels' throughput against beside the
+ * published peaks.  Both run a few milliseconds of work on `stream`, then
+ * synchronise it (unlike every function above, they block the caller).
+ *
+ * conv3d_calibrate_mfma: v_mfma_f32_32x32x16_f16 chains on every CU (8 waves
+ * per CU, fp16 operands from a fixed pseudo-random pattern rotated every
+ * instruction); *tflops is the dense fp16 rate reached, *sclk_mhz the mean
+ * shader clock over the run (shader-clock counter against the 100 MHz
+ * reference counter).  scratch: device memory of at least
+ * conv3d_calibrate_scratch_bytes(), 16-byte aligned, overwritten.
+ * conv3d_calibrate_hbm: a read-only pass over src and a copy src -> dst of
+ * `bytes` (a positive multiple of 16; use well above the 256 MB last-level
+ * cache) with 16-byte non-temporal accesses; *read_gbs and *copy_gbs in GB/s,
+ * the copy counting read + write bytes.  dst is overwritten.
+ * Errors: INVALID_ARG (null outputs, misaligned or overlapping buffers, bad
+ * size), WORKSPACE (scratch too small), HIP.
+ */
+size_t conv3d_calibrate_scratch_bytes(void);
+conv3d_status conv3d_calibrate_mfma(void *scratch, size_t scratch_bytes, double *tflops, double *sclk_mhz,
+                                    void *stream);
+conv3d_status conv3d_calibrate_hbm(const void *src, void *dst, size_t bytes, double *read_gbs, double *copy_gbs,
+                                   void *stream);
 
 /* Static text for a status code. */
 const char *conv3d_status_str(conv3d_status s);

@@ -188,3 +188,28 @@ def test_groupnorm_argument_checks():
     assert gn(x=A + 8) == c3d.CONV3D_ERR_INVALID_ARG
     assert gn(y=A + 1024) == c3d.CONV3D_ERR_INVALID_ARG           # partial overlap
     assert gn(wsb=8) == c3d.CONV3D_ERR_WORKSPACE
+
+
+def test_calibration_argument_checks():
+    import ctypes
+    lib = c3d.load_library()
+    need = c3d.conv3d_calibrate_scratch_bytes()
+    assert need >= 64 * 1024
+    d1, d2 = ctypes.c_double(), ctypes.c_double()
+    r1, r2 = ctypes.byref(d1), ctypes.byref(d2)
+    assert lib.conv3d_calibrate_mfma(A, need, None, r2, None) == c3d.CONV3D_ERR_INVALID_ARG
+    assert lib.conv3d_calibrate_mfma(A + 4, need, r1, r2, None) == c3d.CONV3D_ERR_INVALID_ARG
+    assert lib.conv3d_calibrate_mfma(A, need - 16, r1, r2, None) == c3d.CONV3D_ERR_WORKSPACE
+    assert lib.conv3d_calibrate_hbm(A, A + 512 * MB, 100, r1, r2, None) == c3d.CONV3D_ERR_INVALID_ARG
+    assert lib.conv3d_calibrate_hbm(A, A + 64, 1024, r1, r2, None) == c3d.CONV3D_ERR_INVALID_ARG  # overlap
+    assert lib.conv3d_calibrate_hbm(A, A + 512 * MB, 1024, None, r2, None) == c3d.CONV3D_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="host without a GPU only")
+def test_calibration_without_a_device_reports_no_device():
+    import ctypes
+    lib = c3d.load_library()
+    d1, d2 = ctypes.c_double(), ctypes.c_double()
+    need = c3d.conv3d_calibrate_scratch_bytes()
+    assert lib.conv3d_calibrate_mfma(A, need, ctypes.byref(d1), ctypes.byref(d2), None) == \
+        c3d.CONV3D_ERR_NO_DEVICE
