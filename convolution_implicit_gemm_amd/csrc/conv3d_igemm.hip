@@ -126,44 +126,76 @@ __device__ __forceinline__ void dma16(buf_rsrc r, char *lds, uint32_t voff, uint
 // Offset that is always past a buffer's record count (records stay below 2^30).
 constexpr uint32_t kOOB = 0x80000000u;
 
+// 8-byte buffer load / store (four fp16); out-of-range loads read zeros and
+// out-of-range stores are dropped by the buffer unit's range check.
+__device__ __forceinline__ half4_t load8(buf_rsrc r, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+#else
+    (void)r;
+    (void)off;
+    return half4_t{};
+#endif
+}
+__device__ __forceinline__ void store8(buf_rsrc r, uint32_t off, half4_t v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
+#else
+    (void)r;
+    (void)off;
+    (void)v;
+#endif
+}
+
 // Epilogue of one tile: + bias (+ residual) in fp32, one RNE rounding, NDHWC
 // store.  Lane holds, for sub-tile (i, j) and register 4g+e: channel
 // co = 8g + 4*(lane/32) + e of the sub-tile, voxel m = lane % 32.
+// Branch-free, through buffer resources over this tile's output rows (and the
+// same rows of the residual, and the bias): rows past M lie past the records,
+// channels past Cout get an out-of-range offset, a missing bias or residual is
+// a resource of zero records; out-of-range loads read zeros and such stores
+// are dropped.  The bias and residual of sub-tile row i+1 are loaded before
+// the stores of row i: y aliases neither input, but the compiler cannot know
+// that, and loads queued behind stores would each wait out a round trip.
 template <int TN, int TM, int WN, int WM>
-__device__ __forceinline__ void store_tile(const ConvParams &p, const f32x16 (&acc)[TN][TM], int m0, int n0, int wmi,
-                                           int wni, int rrow, int rhi) {
+__device__ __forceinline__ void store_tile(const ConvParams &p, const f32x16 (&acc)[TN][TM], int m0, int bm, int n0,
+                                           int wmi, int wni, int rrow, int rhi) {
     const int M = (int)p.M;
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
+    const int rows = M - m0 < bm ? M - m0 : bm;
+    const uint32_t tile_bytes = (uint32_t)rows * (uint32_t)p.Cout * 2u;
+    const buf_rsrc ry = make_rsrc(p.y + (int64_t)m0 * p.Cout, tile_bytes);
+    const buf_rsrc rr = make_rsrc(p.res ? p.res + (int64_t)m0 * p.Cout : p.y, p.res ? tile_bytes : 0u);
+    const buf_rsrc rb = make_rsrc(p.bias ? p.bias : p.y, p.bias ? (uint32_t)p.Cout * 2u : 0u);
+    auto offset = [&](int i, int g, int j) {
+        const int co = n0 + wni * WN + i * 32 + 8 * g + 4 * rhi;
+        const int mr = wmi * WM + j * 32 + rrow;  // row within the tile
+        return co < p.Cout ? ((uint32_t)mr * (uint32_t)p.Cout + (uint32_t)co) * 2u : kOOB;
+    };
+    half4_t bv[2][4], rv[2][4][TM];
+    auto fetch = [&](int i, int slot) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int co = n0 + wni * WN + i * 32 + 8 * g + 4 * rhi;
-            if (co >= p.Cout) continue;
-            f32x4 bv = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (p.bias) {
-                const half4_t b4 = *reinterpret_cast<const half4_t *>(p.bias + co);
+            bv[slot][g] = load8(rb, (uint32_t)co * 2u);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) bv[e] = (float)b4[e];
-            }
+            for (int j = 0; j < TM; ++j) rv[slot][g][j] = load8(rr, offset(i, g, j));
+        }
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+        if (i + 1 < TN) fetch(i + 1, (i + 1) & 1);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
             for (int j = 0; j < TM; ++j) {
-                const int m = m0 + wmi * WM + j * 32 + rrow;
-                if (m >= M) continue;
-                const int64_t o = (int64_t)m * p.Cout + co;
-                f32x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] + bv[e];
-                if (p.res) {
-                    const half4_t r4 = *reinterpret_cast<const half4_t *>(p.res + o);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] += (float)r4[e];
-                }
                 half4_t h;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[e];
-                *reinterpret_cast<half4_t *>(p.y + o) = h;
+                for (int e = 0; e < 4; ++e)
+                    h[e] = (_Float16)(acc[i][j][4 * g + e] + (float)bv[i & 1][g][e] + (float)rv[i & 1][g][j][e]);
+                store8(ry, offset(i, g, j), h);
             }
-        }
     }
 }
 
@@ -508,7 +540,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
                 }
         return;
     }
-    store_tile<TN, TM, WN, WM>(p, acc, m0, n0, wmi, wni, rrow, rhi);
+    store_tile<TN, TM, WN, WM>(p, acc, m0, BM, n0, wmi, wni, rrow, rhi);
 }
 
 // Sums the K-pieces of the split tiles and applies the epilogue.  Flat over

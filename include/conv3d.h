@@ -112,7 +112,7 @@ typedef struct {
  * Errors: INVALID_ARG for null pointers, non-positive extents, negative or
  * too-large padding (a pad must be smaller than its kernel extent), an empty
  * output, or an unknown t_pad_mode / flag bit; UNSUPPORTED for c_in or c_out
- * not a multiple of 8, kernel extents above 7, spatial extents above 8192,
+ * not a multiple of 8 or above 65536, kernel extents above 7, spatial extents above 8192,
  * 2^30 or more input or output voxels, weights of 1 GiB or more, or frames
  * so large that the input rows one output tile reads span 1 GiB.
  * The plan may split the K range of the tiles that do not fill a whole wave
