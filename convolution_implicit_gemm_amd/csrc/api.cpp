@@ -97,7 +97,7 @@ Decomp decompose(const c3d::TileCfg &t, int64_t tiles, int niter, int mode) {
     const int64_t full = tiles / kCUs, rem = tiles % kCUs;
     if (mode < 0 || occ != 1 || rem == 0) return best;
     Decomp split = {0, 0, 0, 0.0};
-    for (int pieces = 2; pieces <= 16 && pieces * 4 <= niter; ++pieces) {
+    for (int pieces = 2; pieces <= c3d::kMaxSplitPieces && pieces * 4 <= niter; ++pieces) {
         const size_t ws = (size_t)rem * pieces * t.bm * t.bn * 4;
         if (ws > kMaxSplitWorkspace) break;
         const int64_t waves2 = (rem * pieces + kCUs - 1) / kCUs;

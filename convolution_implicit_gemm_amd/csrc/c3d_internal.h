@@ -34,6 +34,10 @@ struct ConvParams {
     int64_t tiles;         // m_tiles*n_tiles
 };
 
+// Most K-pieces a split tile may be cut into (the fixup kernel loads them all
+// at once).
+constexpr int kMaxSplitPieces = 16;
+
 // Largest input window, in voxels, that one tile of bm output rows can read
 // (the kernel addresses it through one buffer resource with 32-bit offsets).
 int64_t tile_window_voxels(const ConvParams &q, int bm);

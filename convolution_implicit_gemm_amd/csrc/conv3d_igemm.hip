@@ -559,24 +559,23 @@ __global__ __launch_bounds__(256) void conv3d_fixup_kernel(ConvParams p) {
     const int mt = tile / p.n_tiles, nt = tile - mt * p.n_tiles;
     const int co = nt * BN + (wave % NWN) * WN + i * 32 + 8 * g + 4 * (lane >> 5);
     const int m = mt * BM + (wave / NWN) * WM + j * 32 + (lane & 31);
-    const f32x4 *pp = reinterpret_cast<const f32x4 *>(p.partial) + (size_t)t * p.sk_pieces * UNITS + u;
-    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int piece = 0; piece < p.sk_pieces; ++piece) v += pp[(size_t)piece * UNITS];
     if (co >= p.Cout || m >= (int)p.M) return;
-    if (p.bias) {
-        const half4_t b4 = *reinterpret_cast<const half4_t *>(p.bias + co);
+    // every load first (all pieces, bias, residual), then the sum in piece order
+    const f32x4 *pp = reinterpret_cast<const f32x4 *>(p.partial) + (size_t)t * p.sk_pieces * UNITS + u;
+    __builtin_assume(p.sk_pieces >= 2 && p.sk_pieces <= kMaxSplitPieces);
+    f32x4 e[kMaxSplitPieces];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += (float)b4[e];
-    }
+    for (int q = 0; q < kMaxSplitPieces; ++q) e[q] = q < p.sk_pieces ? pp[(size_t)q * UNITS] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const int64_t o = (int64_t)m * p.Cout + co;
-    if (p.res) {
-        const half4_t r4 = *reinterpret_cast<const half4_t *>(p.res + o);
+    const half4_t b4 = p.bias ? *reinterpret_cast<const half4_t *>(p.bias + co) : half4_t{};
+    const half4_t r4 = p.res ? *reinterpret_cast<const half4_t *>(p.res + o) : half4_t{};
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += (float)r4[e];
-    }
+    for (int q = 0; q < kMaxSplitPieces; ++q)
+        if (q < p.sk_pieces) v += e[q];
     half4_t h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[e];
+    for (int c = 0; c < 4; ++c) h[c] = (_Float16)(v[c] + (float)b4[c] + (float)r4[c]);
     *reinterpret_cast<half4_t *>(p.y + o) = h;
 }
 
