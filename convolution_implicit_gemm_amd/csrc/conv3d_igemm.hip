@@ -485,6 +485,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
     constexpr int WAIT_FIRST = (STAGES - 1) * (LW + LAm);
     constexpr int WAIT_LOOP = (STAGES - 2) * (LW + LAm) + D * LAm;
     using all_loads = std::integral_constant<int, -1>;
+    // A wave issuing global->LDS loads runs at raised priority, so that its
+    // loads leave quickly instead of queueing behind the other wave's MFMAs
+    // on the same SIMD (measured: +3% on the steady-state shape).
+    auto raise_prio = [] { __builtin_amdgcn_s_setprio(1); };
+    auto lower_prio = [] { __builtin_amdgcn_s_setprio(0); };
 
     // prologue: stages 0..STAGES-1, wait for stage 0, read its first k-step
 #pragma unroll
@@ -504,15 +509,21 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
         // region A: k-steps 1..KS-1 of this stage are read, 0..KS-2 multiplied
         static_for<KS - 1>([&](auto kk) {
             read_frags(wbuf, abuf, kk + 1, (kk + 1) & 1);
-            if constexpr (D == 1) fire_a(afill, kk);
+            if constexpr (D == 1) {
+                raise_prio();
+                fire_a(afill, kk);
+                lower_prio();
+            }
             mfmas(kk & 1);
         });
         // stage it+1 has landed and every wave is done reading stage it
         wait_lds_and_loads<WAIT_LOOP>();
         // region B: refill this stage's buffers, read k-step 0 of the next
         // stage, and run the last k-step of this one meanwhile
+        raise_prio();
         if constexpr (D == 0) fire_a(abuf, all_loads{});
         fire_w(wbuf);
+        lower_prio();
         advance();
         set_offsets();
         if constexpr (D == 1) afill = abuf;
