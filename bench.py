@@ -297,6 +297,24 @@ def main():
                                           "inputs": "3 copies in rotation"}
         del gx
 
+        # the headline conv with bf16 operands (CONV3D_F_BF16)
+        d1b = workloads.conv_inputs(s1, 1001, dtype="bf16")
+        pb = c3d.conv3d_plan(desc_of(c3d, s1, c3d.CONV3D_F_BIAS | c3d.CONV3D_F_BF16))
+        wsb = ws_for(pb, torch, dev)
+
+        def bfT(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        xb, wb, bb = bfT(d1b["x"]), bfT(d1b["w"]), bfT(d1b["b"])
+        yb = torch.empty(out_dims(s1), dtype=torch.bfloat16, device=dev)
+
+        def conv_bf16():
+            c3d.conv3d_forward(pb, xb, wb, bb, None, yb, wsb)
+        _, p = time_steps(conv_bf16, 50, 20, torch)
+        t = sum(p) / len(p)
+        kern["causal_conv_512_T9_bf16"] = {"ms": round(t, 4), "TFLOP/s": round(pb.info().flops / t / 1e9, 1),
+                                           "kernel": pb.info().kernel_name.decode()}
+        del xb, wb, bb, yb, wsb, d1b
+
         s1f = workloads.CAUSAL_256_T1
         pt1 = c3d.conv3d_plan(desc_of(c3d, s1f, c3d.CONV3D_F_BIAS))
         ws1 = ws_for(pt1, torch, dev)

@@ -28,13 +28,15 @@ CONV3D_TPAD_REPLICATE = 1
 CONV3D_F_BIAS = 1
 CONV3D_F_RESIDUAL = 2
 CONV3D_F_NO_T1_FASTPATH = 4
+CONV3D_F_BF16 = 8
 
 CONV3D_PATH_GENERAL = 0
 CONV3D_PATH_T1_FOLD = 1
 CONV3D_PATH_POINTWISE = 2
 
 EXPORTED = ("conv3d_plan", "conv3d_plan_query", "conv3d_plan_destroy", "conv3d_forward",
-            "groupnorm_silu_workspace", "groupnorm_silu", "conv3d_calibrate_scratch_bytes",
+            "groupnorm_silu_workspace", "groupnorm_silu", "groupnorm_silu_bf16",
+            "conv3d_calibrate_scratch_bytes",
             "conv3d_calibrate_mfma", "conv3d_calibrate_hbm", "conv3d_status_str",
             "conv3d_last_error", "conv3d_version")
 
@@ -91,6 +93,8 @@ def load_library(path: str = LIB_PATH):
     lib.groupnorm_silu_workspace.argtypes = [i32, i64, i32, i32]
     lib.groupnorm_silu_workspace.restype = sz
     lib.groupnorm_silu.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_float, i32, vp, sz, vp]
+    lib.groupnorm_silu_bf16.argtypes = lib.groupnorm_silu.argtypes
+    lib.groupnorm_silu_bf16.restype = ctypes.c_int
     lib.groupnorm_silu.restype = ctypes.c_int
     lib.conv3d_status_str.argtypes = [ctypes.c_int]
     lib.conv3d_status_str.restype = ctypes.c_char_p
@@ -194,13 +198,14 @@ def groupnorm_silu_workspace(n, thw, c, groups) -> int:
 
 
 def groupnorm_silu(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, workspace,
-                   workspace_bytes=None, stream=None) -> None:
+                   workspace_bytes=None, stream=None, bf16=False) -> None:
     """Enqueue y = [SiLU](GroupNorm(x)) on ``stream``."""
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
-    _check(load_library().groupnorm_silu(_addr(x), _addr(gamma), _addr(beta), _addr(y), n, thw, c,
-                                         groups, float(eps), 1 if apply_silu else 0,
-                                         _addr(workspace), workspace_bytes, _stream(stream)))
+    lib = load_library()
+    fn = lib.groupnorm_silu_bf16 if bf16 else lib.groupnorm_silu
+    _check(fn(_addr(x), _addr(gamma), _addr(beta), _addr(y), n, thw, c, groups, float(eps),
+              1 if apply_silu else 0, _addr(workspace), workspace_bytes, _stream(stream)))
 
 
 def conv3d_calibrate_scratch_bytes() -> int:
@@ -223,6 +228,13 @@ def conv3d_calibrate_hbm(src, dst, nbytes, stream=None):
     _check(load_library().conv3d_calibrate_hbm(_addr(src), _addr(dst), nbytes, ctypes.byref(rd),
                                                ctypes.byref(cp), _stream(stream)))
     return rd.value, cp.value
+
+
+def groupnorm_silu_bf16(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, workspace,
+                        workspace_bytes=None, stream=None) -> None:
+    """groupnorm_silu with bf16 x, gamma, beta and y."""
+    groupnorm_silu(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, workspace, workspace_bytes,
+                   stream, bf16=True)
 
 
 def conv3d_status_str(status: int) -> str:

@@ -158,7 +158,7 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
         return fail(CONV3D_ERR_INVALID_ARG, "padding must be smaller than the kernel extent");
     if (d->t_pad_mode != CONV3D_TPAD_ZERO && d->t_pad_mode != CONV3D_TPAD_REPLICATE)
         return fail(CONV3D_ERR_INVALID_ARG, "unknown t_pad_mode %d", d->t_pad_mode);
-    const uint32_t known = CONV3D_F_BIAS | CONV3D_F_RESIDUAL | CONV3D_F_NO_T1_FASTPATH;
+    const uint32_t known = CONV3D_F_BIAS | CONV3D_F_RESIDUAL | CONV3D_F_NO_T1_FASTPATH | CONV3D_F_BF16;
     if (d->flags & ~known) return fail(CONV3D_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags & ~known);
     const int To = d->t + d->pad_t_front + d->pad_t_back - d->kt + 1;
     const int Ho = d->h + 2 * d->pad_h - d->kh + 1;
@@ -217,6 +217,7 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
     q.ph = d->pad_h;
     q.pw = d->pad_w;
     q.replicate = d->t_pad_mode == CONV3D_TPAD_REPLICATE ? 1 : 0;
+    q.bf16 = (d->flags & CONV3D_F_BF16) ? 1 : 0;
     q.K = q.kt * q.kh * q.kw * q.Cin;
     q.M = out_vox;
 
@@ -356,7 +357,8 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
     if (q.sk_tiles) q.partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + p->ws_fold);
     if (p->path == CONV3D_PATH_T1_FOLD) {
         _Float16 *w2 = static_cast<_Float16 *>(workspace);
-        hipError_t e = c3d::launch_fold_taps(q.w, w2, p->d.c_out, p->d.kt, p->fold_khwc, p->fold_lo, p->fold_hi, s);
+        hipError_t e = c3d::launch_fold_taps(q.w, w2, p->d.c_out, p->d.kt, p->fold_khwc, p->fold_lo, p->fold_hi,
+                                             q.bf16 != 0, s);
         if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "fold launch: %s", hipGetErrorString(e));
         q.w = w2;
     }
@@ -370,6 +372,7 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
         pw.Cin = q.Cin;
         pw.Cout = q.Cout;
         pw.M = q.M;
+        pw.bf16 = q.bf16;
         hipError_t e = c3d::launch_pointwise(pw, s);
         if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "pointwise launch: %s", hipGetErrorString(e));
         return ok();
@@ -388,9 +391,9 @@ size_t groupnorm_silu_workspace(int32_t n, int64_t thw, int32_t c, int32_t group
     return c3d::gn_workspace_bytes(n, thw, c, groups);
 }
 
-conv3d_status groupnorm_silu(const void *x, const void *gamma, const void *beta, void *y, int32_t n, int64_t thw,
-                             int32_t c, int32_t groups, float eps, int32_t apply_silu, void *workspace,
-                             size_t workspace_bytes, void *stream) {
+static conv3d_status gn_entry(const void *x, const void *gamma, const void *beta, void *y, int32_t n, int64_t thw,
+                              int32_t c, int32_t groups, float eps, int32_t apply_silu, void *workspace,
+                              size_t workspace_bytes, void *stream, bool bf16) {
     if (!x || !gamma || !beta || !y) return fail(CONV3D_ERR_INVALID_ARG, "x, gamma, beta and y are required");
     if (n < 1 || thw < 1 || c < 1 || groups < 1) return fail(CONV3D_ERR_INVALID_ARG, "sizes must be positive");
     if (c % groups) return fail(CONV3D_ERR_INVALID_ARG, "c (%d) is not a multiple of groups (%d)", c, groups);
@@ -411,9 +414,22 @@ conv3d_status groupnorm_silu(const void *x, const void *gamma, const void *beta,
     if (st != CONV3D_OK) return st;
     hipError_t e = c3d::launch_groupnorm_silu(static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(gamma),
                                               static_cast<const _Float16 *>(beta), static_cast<_Float16 *>(y), n, thw,
-                                              c, groups, eps, apply_silu, workspace, static_cast<hipStream_t>(stream));
+                                              c, groups, eps, apply_silu, bf16, workspace,
+                                              static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "groupnorm launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+conv3d_status groupnorm_silu(const void *x, const void *gamma, const void *beta, void *y, int32_t n, int64_t thw,
+                             int32_t c, int32_t groups, float eps, int32_t apply_silu, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    return gn_entry(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, workspace, workspace_bytes, stream, false);
+}
+
+conv3d_status groupnorm_silu_bf16(const void *x, const void *gamma, const void *beta, void *y, int32_t n,
+                                  int64_t thw, int32_t c, int32_t groups, float eps, int32_t apply_silu,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    return gn_entry(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

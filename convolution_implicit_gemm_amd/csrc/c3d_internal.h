@@ -12,6 +12,7 @@ namespace c3d {
 // argument.  Extents are of the conv as executed (after a temporal fold the
 // kernel sees kt = 1 and T = 1).
 struct ConvParams {
+    // Tensors are 16-bit storage: fp16, or bf16 when bf16 is set.
     const _Float16 *x;     // [N][T][H][W][Cin]
     const _Float16 *w;     // [Cout][kt][kh][kw][Cin]
     const _Float16 *bias;  // [Cout] or null
@@ -32,6 +33,7 @@ struct ConvParams {
     uint32_t w_bytes;      // Cout*K*2, below 2^30
     int64_t M;             // N*To*Ho*Wo, below 2^30
     int64_t tiles;         // m_tiles*n_tiles
+    int32_t bf16;          // elements are bf16 (else fp16)
 };
 
 // Most K-pieces a split tile may be cut into (the fixup kernel loads them all
@@ -59,6 +61,7 @@ const TileCfg *tile_table(int *count);
 
 // 1x1x1 convolution without padding: a streaming GEMM over voxels.
 struct PwParams {
+    // 16-bit storage: fp16, or bf16 when bf16 is set
     const _Float16 *x;     // [M][Cin]
     const _Float16 *w;     // [Cout][Cin]
     const _Float16 *bias;  // [Cout] or null
@@ -66,6 +69,7 @@ struct PwParams {
     _Float16 *y;           // [M][Cout]
     int32_t Cin, Cout;
     int64_t M;
+    int32_t bf16;
 };
 bool pointwise_supported(int32_t cin, int32_t cout);
 hipError_t launch_pointwise(const PwParams &p, hipStream_t s);
@@ -79,15 +83,15 @@ struct PwGeom {
 PwGeom pointwise_geometry(int32_t cin, int32_t cout, int64_t m);
 
 // Sum of the temporal taps tau in [tau_lo, tau_hi] of w [Cout][kt][khw*Cin]
-// into w2 [Cout][khw*Cin], in fp32, rounded once to fp16.
+// into w2 [Cout][khw*Cin], in fp32, rounded once to the element type.
 hipError_t launch_fold_taps(const _Float16 *w, _Float16 *w2, int32_t cout, int32_t kt,
-                            int64_t khw_cin, int32_t tau_lo, int32_t tau_hi, hipStream_t s);
+                            int64_t khw_cin, int32_t tau_lo, int32_t tau_hi, bool bf16, hipStream_t s);
 
 // GroupNorm(+SiLU): workspace layout and launch.
 size_t gn_workspace_bytes(int32_t n, int64_t thw, int32_t c, int32_t groups);
 hipError_t launch_groupnorm_silu(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta,
                                  _Float16 *y, int32_t n, int64_t thw, int32_t c, int32_t groups,
-                                 float eps, int32_t silu, void *ws, hipStream_t s);
+                                 float eps, int32_t silu, bool bf16, void *ws, hipStream_t s);
 
 // Measurement aids (calibrate.hip): machine ceilings for the kernels above.
 size_t calibrate_scratch_bytes();

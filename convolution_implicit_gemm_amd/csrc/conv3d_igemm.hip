@@ -12,7 +12,8 @@
 // for CDNA4, not after any shader.
 //
 // gfx950 design:
-//  * Matrix cores: v_mfma_f32_32x32x16_f16 (fp16 products, fp32 accumulate).
+//  * Matrix cores: v_mfma_f32_32x32x16_f16 or _bf16 (16-bit products, fp32
+//    accumulate), one template per element type.
 //    The MFMA "A" operand is the weight tile (rows = output channels) and the
 //    "B" operand the gathered activations (columns = voxels), so each lane's
 //    accumulators hold 4 consecutive output channels of one voxel: the
@@ -44,6 +45,7 @@
 //  * Workgroups are renumbered so each XCD (workgroup id mod 8) walks a
 //    contiguous range of tiles; tiles sharing input rows then share an L2.
 #include "c3d_internal.h"
+#include "elem16.h"
 
 #include <type_traits>
 
@@ -158,7 +160,7 @@ __device__ __forceinline__ void store8(buf_rsrc r, uint32_t off, half4_t v) {
 // are dropped.  The bias and residual of sub-tile row i+1 are loaded before
 // the stores of row i: y aliases neither input, but the compiler cannot know
 // that, and loads queued behind stores would each wait out a round trip.
-template <int TN, int TM, int WN, int WM>
+template <typename E, int TN, int TM, int WN, int WM>
 __device__ __forceinline__ void store_tile(const ConvParams &p, const f32x16 (&acc)[TN][TM], int m0, int bm, int n0,
                                            int wmi, int wni, int rrow, int rhi) {
     const int M = (int)p.M;
@@ -193,7 +195,7 @@ __device__ __forceinline__ void store_tile(const ConvParams &p, const f32x16 (&a
                 half4_t h;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    h[e] = (_Float16)(acc[i][j][4 * g + e] + (float)bv[i & 1][g][e] + (float)rv[i & 1][g][j][e]);
+                    h[e] = from_f32<E>(acc[i][j][4 * g + e] + to_f32<E>(bv[i & 1][g][e]) + to_f32<E>(rv[i & 1][g][j][e]));
                 store8(ry, offset(i, g, j), h);
             }
     }
@@ -204,7 +206,7 @@ __device__ __forceinline__ void store_tile(const ConvParams &p, const f32x16 (&a
 // the operand that misses L2, is fetched one K-iteration further ahead than
 // the weights, which every tile on an XCD reads at about the same time.
 // TT: kt <= 3, gather offsets from per-tile tables (see set_offsets).
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int ASTAGES, bool TAIL, bool TT>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int ASTAGES, bool TAIL, bool TT, typename E>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kernel(ConvParams p) {
     constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN;
     constexpr int RB = BK * 2;        // bytes per LDS row
@@ -464,7 +466,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
         for (int i = 0; i < TN; ++i)
 #pragma unroll
             for (int j = 0; j < TM; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[slot][i], bf[slot][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = mfma_32x32x16<E>(af[slot][i], bf[slot][j], acc[i][j]);
     };
 
     // Fetch schedule.  Stage k's activations and weights are fetched while
@@ -551,14 +553,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
                 }
         return;
     }
-    store_tile<TN, TM, WN, WM>(p, acc, m0, BM, n0, wmi, wni, rrow, rhi);
+    store_tile<E, TN, TM, WN, WM>(p, acc, m0, BM, n0, wmi, wni, rrow, rhi);
 }
 
 // Sums the K-pieces of the split tiles and applies the epilogue.  Flat over
 // float4 units of the fragment-order partials: unit u of tile t holds the 4
 // channels co = n0 + wni*WN + i*32 + 8g + 4*(lane/32) + e of voxel
 // m = m0 + wmi*WM + j*32 + lane%32, where u = (((wave*TN + i)*TM + j)*4 + g)*64 + lane.
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, typename E>
 __global__ __launch_bounds__(256) void conv3d_fixup_kernel(ConvParams p) {
     constexpr int NWN = BN / WN, TM = WM / 32, TN = WN / 32, UNITS = BM * BN / 4;
     const int64_t g_u = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -586,28 +588,39 @@ __global__ __launch_bounds__(256) void conv3d_fixup_kernel(ConvParams p) {
         if (q < p.sk_pieces) v += e[q];
     half4_t h;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) h[c] = (_Float16)(v[c] + (float)b4[c] + (float)r4[c]);
+    for (int c = 0; c < 4; ++c) h[c] = from_f32<E>(v[c] + to_f32<E>(b4[c]) + to_f32<E>(r4[c]));
     *reinterpret_cast<half4_t *>(p.y + o) = h;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int ASTAGES, bool TAIL, typename E>
+void launch_igemm_e(const ConvParams &p, hipStream_t s) {
+    constexpr int threads = (BM / WM) * (BN / WN) * 64;
+    const unsigned grid = (unsigned)(p.dp_tiles + p.sk_tiles * p.sk_pieces);
+    if (p.kt <= 3)
+        hipLaunchKernelGGL((conv3d_igemm_kernel<BM, BN, BK, WM, WN, STAGES, ASTAGES, TAIL, true, E>), dim3(grid),
+                           dim3(threads), 0, s, p);
+    else
+        hipLaunchKernelGGL((conv3d_igemm_kernel<BM, BN, BK, WM, WN, STAGES, ASTAGES, TAIL, false, E>), dim3(grid),
+                           dim3(threads), 0, s, p);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int ASTAGES, bool TAIL>
 hipError_t launch_igemm(const ConvParams &p, hipStream_t s) {
-    constexpr int threads = (BM / WM) * (BN / WN) * 64;
-    const unsigned grid = (unsigned)(p.dp_tiles + p.sk_tiles * p.sk_pieces);
-    if (p.kt <= 3)
-        hipLaunchKernelGGL((conv3d_igemm_kernel<BM, BN, BK, WM, WN, STAGES, ASTAGES, TAIL, true>), dim3(grid),
-                           dim3(threads), 0, s, p);
+    if (p.bf16)
+        launch_igemm_e<BM, BN, BK, WM, WN, STAGES, ASTAGES, TAIL, __bf16>(p, s);
     else
-        hipLaunchKernelGGL((conv3d_igemm_kernel<BM, BN, BK, WM, WN, STAGES, ASTAGES, TAIL, false>), dim3(grid),
-                           dim3(threads), 0, s, p);
+        launch_igemm_e<BM, BN, BK, WM, WN, STAGES, ASTAGES, TAIL, _Float16>(p, s);
     return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_fixup(const ConvParams &p, hipStream_t s) {
     const int64_t units = (int64_t)p.sk_tiles * (BM * BN / 4);
-    hipLaunchKernelGGL((conv3d_fixup_kernel<BM, BN, WM, WN>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s,
-                       p);
+    const dim3 grid((unsigned)((units + 255) / 256));
+    if (p.bf16)
+        hipLaunchKernelGGL((conv3d_fixup_kernel<BM, BN, WM, WN, __bf16>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((conv3d_fixup_kernel<BM, BN, WM, WN, _Float16>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -655,9 +668,9 @@ const TileCfg *tile_table(int *count) {
 // that frame, so the causal 3D correlation equals a 2D one whose kernel is
 // the sum of the temporal taps ("Video VAE" section of the Qwen Image post,
 // Draw Things engineering feed).  Summed in fp32, rounded once.
-__global__ __launch_bounds__(256) void fold_taps_kernel(const _Float16 *__restrict__ w,
-                                                        _Float16 *__restrict__ w2, int32_t cout,
-                                                        int32_t kt, int64_t khwc, int32_t lo,
+template <typename E>
+__global__ __launch_bounds__(256) void fold_taps_kernel(const _Float16 *__restrict__ w, _Float16 *__restrict__ w2,
+                                                        int32_t cout, int32_t kt, int64_t khwc, int32_t lo,
                                                         int32_t hi) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t total8 = (int64_t)cout * khwc / 8;
@@ -668,20 +681,24 @@ __global__ __launch_bounds__(256) void fold_taps_kernel(const _Float16 *__restri
     for (int tau = lo; tau <= hi; ++tau) {
         const half8_t v = *reinterpret_cast<const half8_t *>(w + (co * kt + tau) * khwc + e);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] += (float)v[q];
+        for (int q = 0; q < 8; ++q) acc[q] += to_f32<E>(v[q]);
     }
     half8_t o;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) o[q] = (_Float16)acc[q];
+    for (int q = 0; q < 8; ++q) o[q] = from_f32<E>(acc[q]);
     *reinterpret_cast<half8_t *>(w2 + e8) = o;
 }
 
 hipError_t launch_fold_taps(const _Float16 *w, _Float16 *w2, int32_t cout, int32_t kt, int64_t khw_cin,
-                            int32_t tau_lo, int32_t tau_hi, hipStream_t s) {
+                            int32_t tau_lo, int32_t tau_hi, bool bf16, hipStream_t s) {
     const int64_t total8 = (int64_t)cout * khw_cin / 8;
     const unsigned blocks = (unsigned)((total8 + 255) / 256);
-    hipLaunchKernelGGL(fold_taps_kernel, dim3(blocks), dim3(256), 0, s, w, w2, cout, kt, khw_cin, tau_lo,
-                       tau_hi);
+    if (bf16)
+        hipLaunchKernelGGL(fold_taps_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, w, w2, cout, kt, khw_cin, tau_lo,
+                           tau_hi);
+    else
+        hipLaunchKernelGGL(fold_taps_kernel<_Float16>, dim3(blocks), dim3(256), 0, s, w, w2, cout, kt, khw_cin,
+                           tau_lo, tau_hi);
     return hipGetLastError();
 }
 

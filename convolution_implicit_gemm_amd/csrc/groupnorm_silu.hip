@@ -22,6 +22,7 @@
 //          y*sigmoid(y), rounded once to fp16, with the next batch of loads
 //          in flight while a batch is converted.
 #include "c3d_internal.h"
+#include "elem16.h"
 
 namespace c3d {
 
@@ -92,6 +93,7 @@ __device__ __forceinline__ Welford chan_merge(Welford a, Welford b) {
     return r;
 }
 
+template <typename E>
 __global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(const _Float16 *__restrict__ x, int64_t thw,
                                                                 int32_t c, int32_t groups, int32_t sb,
                                                                 float4 *__restrict__ part) {
@@ -112,11 +114,11 @@ __global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(const _Float16 *_
     // these loads leave it in the MALL.
     float s1 = 0.0f, s2 = 0.0f, cnt = 0.0f;
     int64_t v = v_begin + tid / vpv;
-    const float K = v < v_end ? (float)xs[v * vpv + vi][0] : 0.0f;
+    const float K = v < v_end ? to_f32<E>(xs[v * vpv + vi][0]) : 0.0f;
     auto accumulate = [&](const half8_t h) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const float d = (float)h[q] - K;
+            const float d = to_f32<E>(h[q]) - K;
             s1 += d;
             s2 = fmaf(d, d, s2);
         }
@@ -177,6 +179,7 @@ __global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(const _Float16 *_
 
 constexpr int kFinalThreads = 256;
 
+template <typename E>
 __global__ __launch_bounds__(kFinalThreads) void gn_final_kernel(const float4 *__restrict__ part, int32_t sb,
                                                                  int32_t c, int32_t groups, float eps,
                                                                  const _Float16 *__restrict__ gamma,
@@ -221,9 +224,9 @@ __global__ __launch_bounds__(kFinalThreads) void gn_final_kernel(const float4 *_
     const int cg = c / groups;
     for (int cc = tid; cc < cg; cc += kFinalThreads) {
         const int ch = g * cg + cc;
-        const float a = stat.y * (float)gamma[ch];
+        const float a = stat.y * to_f32<E>(gamma[ch]);
         scale[(size_t)n * c + ch] = a;
-        shift[(size_t)n * c + ch] = (float)beta[ch] - stat.x * a;
+        shift[(size_t)n * c + ch] = to_f32<E>(beta[ch]) - stat.x * a;
     }
 }
 
@@ -233,7 +236,7 @@ __device__ __forceinline__ float silu_f32(float y) {
     return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-template <bool SILU>
+template <bool SILU, typename E>
 __global__ __launch_bounds__(kMaxThreads) void gn_apply_kernel(const _Float16 *__restrict__ x,
                                                               _Float16 *__restrict__ y, int64_t thw,
                                                               int32_t c, const float *__restrict__ scale,
@@ -256,9 +259,9 @@ __global__ __launch_bounds__(kMaxThreads) void gn_apply_kernel(const _Float16 *_
         half8_t o;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            float t = fmaf((float)h[q], a[q], bsh[q]);
+            float t = fmaf(to_f32<E>(h[q]), a[q], bsh[q]);
             if (SILU) t = silu_f32(t);
-            o[q] = (_Float16)t;
+            o[q] = from_f32<E>(t);
         }
         return o;
     };
@@ -288,6 +291,30 @@ __global__ __launch_bounds__(kMaxThreads) void gn_apply_kernel(const _Float16 *_
     for (; v < thw; v += vox_step) __builtin_nontemporal_store(apply(__builtin_nontemporal_load(xs + v * vpv + vi)), ys + v * vpv + vi);
 }
 
+template <typename E>
+hipError_t launch_gn(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta, _Float16 *y, int32_t n,
+                     int64_t thw, int32_t c, int32_t groups, float eps, int32_t silu, void *ws, hipStream_t s) {
+    const GnGeom g = gn_geom(n, thw, c);
+    char *base = static_cast<char *>(ws);
+    float *scale = reinterpret_cast<float *>(base);
+    float *shift = scale + (size_t)n * c;
+    float4 *part = reinterpret_cast<float4 *>(base + off_part(n, c));
+    hipLaunchKernelGGL(gn_stats_kernel<E>, dim3(g.sb, n), dim3(g.sthreads), 0, s, x, thw, c, groups, g.sb, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gn_final_kernel<E>, dim3(groups, n), dim3(kFinalThreads), 0, s, part, g.sb, c, groups, eps,
+                       gamma, beta, scale, shift);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (silu)
+        hipLaunchKernelGGL((gn_apply_kernel<true, E>), dim3(g.ab, n), dim3(g.athreads), 0, s, x, y, thw, c, scale,
+                           shift);
+    else
+        hipLaunchKernelGGL((gn_apply_kernel<false, E>), dim3(g.ab, n), dim3(g.athreads), 0, s, x, y, thw, c, scale,
+                           shift);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t gn_workspace_bytes(int32_t n, int64_t thw, int32_t c, int32_t groups) {
@@ -296,27 +323,10 @@ size_t gn_workspace_bytes(int32_t n, int64_t thw, int32_t c, int32_t groups) {
 }
 
 hipError_t launch_groupnorm_silu(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta, _Float16 *y,
-                                 int32_t n, int64_t thw, int32_t c, int32_t groups, float eps, int32_t silu,
+                                 int32_t n, int64_t thw, int32_t c, int32_t groups, float eps, int32_t silu, bool bf16,
                                  void *ws, hipStream_t s) {
-    const GnGeom g = gn_geom(n, thw, c);
-    char *base = static_cast<char *>(ws);
-    float *scale = reinterpret_cast<float *>(base);
-    float *shift = scale + (size_t)n * c;
-    float4 *part = reinterpret_cast<float4 *>(base + off_part(n, c));
-    hipLaunchKernelGGL(gn_stats_kernel, dim3(g.sb, n), dim3(g.sthreads), 0, s, x, thw, c, groups, g.sb, part);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gn_final_kernel, dim3(groups, n), dim3(kFinalThreads), 0, s, part, g.sb, c, groups, eps,
-                       gamma, beta, scale, shift);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (silu)
-        hipLaunchKernelGGL(gn_apply_kernel<true>, dim3(g.ab, n), dim3(g.athreads), 0, s, x, y, thw, c, scale,
-                           shift);
-    else
-        hipLaunchKernelGGL(gn_apply_kernel<false>, dim3(g.ab, n), dim3(g.athreads), 0, s, x, y, thw, c, scale,
-                           shift);
-    return hipGetLastError();
+    if (bf16) return launch_gn<__bf16>(x, gamma, beta, y, n, thw, c, groups, eps, silu, ws, s);
+    return launch_gn<_Float16>(x, gamma, beta, y, n, thw, c, groups, eps, silu, ws, s);
 }
 
 }  // namespace c3d

@@ -19,6 +19,7 @@
 // Loads and stores share one counter on gfx9; the per-tile wait counts only
 // the loads issued after the tile's own, which loads retire in order.
 #include "c3d_internal.h"
+#include "elem16.h"
 
 namespace c3d {
 
@@ -89,7 +90,7 @@ constexpr int pw_ring() {
     return nb > 8 ? 8 : (nb < 2 ? 2 : nb);
 }
 
-template <int CIN>
+template <int CIN, typename E>
 __global__ __launch_bounds__(256, 2) void pointwise_kernel(PwParams p) {
     constexpr int RB = CIN * 2;                 // bytes per input row
     constexpr int CPR = CIN / 8;                // 16-byte chunks per row
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(256, 2) void pointwise_kernel(PwParams p) {
         pw_half4 b4 = {};
         if (p.bias && live) b4 = *reinterpret_cast<const pw_half4 *>(p.bias + co0 + 8 * g + 4 * rhi);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bv[g][e] = (float)b4[e];
+        for (int e = 0; e < 4; ++e) bv[g][e] = to_f32<E>(b4[e]);
     }
 
     const int M = (int)p.M;
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void pointwise_kernel(PwParams p) {
 #pragma unroll
             for (int u = 0; u < SUB; ++u) {
                 const pw_half8 b = *reinterpret_cast<const pw_half8 *>(sb + u * 32 * RB + koff[f]);
-                acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[f], b, acc[u], 0, 0, 0);
+                acc[u] = mfma_32x32x16<E>(wf[f], b, acc[u]);
             }
         }
         // epilogue: + bias (+ residual) in fp32 and one RNE rounding in registers,
@@ -204,11 +205,11 @@ __global__ __launch_bounds__(256, 2) void pointwise_kernel(PwParams p) {
                 if (p.res && m0 + vrow < M) {
                     const pw_half4 r4 = *reinterpret_cast<const pw_half4 *>(p.res + (int64_t)(m0 + vrow) * p.Cout + co);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] += (float)r4[e];
+                    for (int e = 0; e < 4; ++e) v[e] += to_f32<E>(r4[e]);
                 }
                 pw_half4 h;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[e];
+                for (int e = 0; e < 4; ++e) h[e] = from_f32<E>(v[e]);
                 // 8-byte unit (2g + rhi) of the 64-byte row, xor-swizzled by the row
                 *reinterpret_cast<pw_half4 *>(ob + vrow * 64 + (((2 * g + rhi) ^ (vrow & 7)) * 8)) = h;
             }
@@ -253,8 +254,11 @@ PwGeom pw_geom(int32_t cout, int64_t m) {
 template <int CIN>
 hipError_t launch_pw(const PwParams &p, hipStream_t s) {
     const PwGeom g = pw_geom<CIN>(p.Cout, p.M);
-    hipLaunchKernelGGL(pointwise_kernel<CIN>, dim3((unsigned)g.grid_x, (unsigned)g.grid_y), dim3(64 * kPwWaves), 0, s,
-                       p);
+    const dim3 grid((unsigned)g.grid_x, (unsigned)g.grid_y);
+    if (p.bf16)
+        hipLaunchKernelGGL((pointwise_kernel<CIN, __bf16>), grid, dim3(64 * kPwWaves), 0, s, p);
+    else
+        hipLaunchKernelGGL((pointwise_kernel<CIN, _Float16>), grid, dim3(64 * kPwWaves), 0, s, p);
     return hipGetLastError();
 }
 

@@ -22,7 +22,9 @@
  *    framework's current stream without its own commit.
  *  - The caller owns every device buffer.  The library never allocates
  *    device memory.  Device pointers must be 16-byte aligned.
- *  - All tensors are fp16 (IEEE binary16) unless stated; accumulation is fp32.
+ *  - All tensors are fp16 (IEEE binary16), or bf16 (the upper half of an IEEE
+ *    binary32) where stated; accumulation is fp32 and each output is
+ *    rounded once, to nearest even.
  *  - On failure a status other than CONV3D_OK is returned, nothing is
  *    launched, and conv3d_last_error() holds a message for this thread.
  */
@@ -55,7 +57,8 @@ typedef enum {
 enum {
     CONV3D_F_BIAS = 1u,            /* add bias[Cout] */
     CONV3D_F_RESIDUAL = 2u,        /* add residual[N,To,Ho,Wo,Cout] (fp32 add, one rounding) */
-    CONV3D_F_NO_T1_FASTPATH = 4u   /* never fold temporal taps, even when it is exact */
+    CONV3D_F_NO_T1_FASTPATH = 4u,  /* never fold temporal taps, even when it is exact */
+    CONV3D_F_BF16 = 8u             /* x, weight, bias, residual and y are bf16, not fp16 */
 };
 
 /* Execution paths a plan may choose. */
@@ -167,6 +170,11 @@ conv3d_status groupnorm_silu(const void *x, const void *gamma, const void *beta,
                              int32_t n, int64_t thw, int32_t c, int32_t groups, float eps,
                              int32_t apply_silu, void *workspace, size_t workspace_bytes,
                              void *stream);
+/* The same with x, gamma, beta and y in bf16 (same workspace size). */
+conv3d_status groupnorm_silu_bf16(const void *x, const void *gamma, const void *beta, void *y,
+                                  int32_t n, int64_t thw, int32_t c, int32_t groups, float eps,
+                                  int32_t apply_silu, void *workspace, size_t workspace_bytes,
+                                  void *stream);
 
 /*
  * Measurement aids, not on the convolution path: the ceilings of the machine

@@ -21,6 +21,9 @@ Function inventory and pins (tests/test_oracle_*.py):
   groupnorm_silu    -- pinned: torch.nn.functional.group_norm (fp64, CPU) +
                        SiLU; closed forms (constant group, +-a halves);
                        per-sample independence; shift/scale invariance.
+  bf16_to_f64       -- pinned: every one of the 65,536 patterns against the
+                       value sign * 2^(e-127) * (1 + f/128) (normal) or
+                       sign * 2^-126 * f/128 (subnormal) built term by term.
   decoder_block     -- a composition of the two above.  Its end-to-end
                        tolerance is not fixed by the pages: parity unpinned
                        beyond the pins of its parts.
@@ -143,6 +146,17 @@ def _maybe_f16(a):
 def f16_to_f64(bits: int) -> float:
     """The oracle's exact binary16 decoder (exposed for its pin)."""
     return _load().oracle_f16_to_f64(bits)
+
+
+def bf16_to_f64(bits):
+    """Exact values of bf16 bit patterns (uint16 array) as float64.
+
+    bf16 is the upper half of an IEEE binary32: widening the pattern by 16 zero
+    bits gives the binary32 of the same value, which float64 holds exactly.
+    """
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns widen to quiet NaNs
+        return b.view(np.float32).astype(np.float64)
 
 
 def conv3d_points(x, w, b, res, pads, tmode, m_idx, co_idx):

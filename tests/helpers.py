@@ -9,6 +9,10 @@ The acceptance bounds (stated once here, used by every GPU test):
                    rounding costs half an ulp.
   groupnorm_silu:  |gpu - ref| <= 1e-3 * |ref| + 2^-14 (the absolute floor,
                    the smallest fp16 normal, covers SiLU's zero crossing).
+bf16 outputs (8 significant bits): the same with the bf16 ulp in place of the
+fp16 one (conv), or added (GroupNorm, whose relative term is below half a bf16
+ulp); the T=1 fold of bf16 weights adds 2^-9 * S (its one rounding), so the fold
+path of bf16 uses 3e-3 * S.
 """
 from __future__ import annotations
 
@@ -25,16 +29,24 @@ GUARD_BITS = 0x7E5A  # a NaN pattern no kernel writes
 
 
 def dev(a):
-    """numpy fp16 -> torch fp16 on cuda:0."""
-    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    """numpy fp16 -> torch fp16 on cuda:0; numpy uint16 (bf16 bits) -> torch bfloat16."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(a).to("cuda:0")
 
 
-def guarded_empty(shape):
-    """(buffer, view): an fp16 device tensor with NaN-patterned guard bands around it."""
+def host_bits(t):
+    """torch bfloat16 tensor -> numpy uint16 bits on the host."""
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def guarded_empty(shape, dtype=torch.float16):
+    """(buffer, view): a 16-bit device tensor with guard bands of a fixed pattern around it."""
     n = int(np.prod(shape))
     buf = torch.empty(n + 2 * GUARD, dtype=torch.int16, device="cuda:0")
     buf.fill_(GUARD_BITS - 65536 if GUARD_BITS > 32767 else GUARD_BITS)
-    view = buf[GUARD:GUARD + n].view(torch.float16).view(shape)
+    view = buf[GUARD:GUARD + n].view(dtype).view(shape)
     return buf, view
 
 
@@ -103,10 +115,15 @@ def out_dims(shape):
 
 
 def run_conv(shape, x, w, b=None, res=None, flags=0, tile=None, keep_device=False, split=None):
-    """Run the HIP conv through the C ABI; returns (y fp16 numpy or device tensor, plan info).
+    """Run the HIP conv through the C ABI; returns (y numpy or device tensor, plan info).
 
+    fp16 inputs give an fp16 result; uint16 inputs are bf16 bits (the plan gets
+    CONV3D_F_BF16) and the result is uint16 bits too.
     split: None lets the planner decide on K-splitting; "0" forbids it, "1" forces it.
     """
+    bf16 = (x.dtype == torch.bfloat16) if isinstance(x, torch.Tensor) else (np.asarray(x).dtype == np.uint16)
+    if bf16:
+        flags |= c3d.CONV3D_F_BF16
     if b is not None:
         flags |= c3d.CONV3D_F_BIAS
     if res is not None:
@@ -118,13 +135,13 @@ def run_conv(shape, x, w, b=None, res=None, flags=0, tile=None, keep_device=Fals
     wd = w if isinstance(w, torch.Tensor) else dev(w)
     bd = None if b is None else (b if isinstance(b, torch.Tensor) else dev(b))
     rd = None if res is None else (res if isinstance(res, torch.Tensor) else dev(res))
-    buf, y = guarded_empty(out_dims(shape))
+    buf, y = guarded_empty(out_dims(shape), torch.bfloat16 if bf16 else torch.float16)
     c3d.conv3d_forward(plan, xd, wd, bd, rd, y, workspace_for(plan))
     torch.cuda.synchronize()
     check_guards(buf)
     if keep_device:
         return y, info
-    return y.cpu().numpy(), info
+    return (host_bits(y) if bf16 else y.cpu().numpy()), info
 
 
 def ulp16(v):
@@ -135,18 +152,30 @@ def ulp16(v):
     return np.exp2(e - 10)
 
 
-def conv_violations(gpu, ref, mag):
-    """Indices where the conv bound fails, and the worst ratio err / bound."""
+def ulp_bf16(v):
+    """bf16 spacing at v: 8 significant bits, normal range down to 2^-126."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.where(a > 0, np.maximum(e, -126), -126)
+    return np.exp2(e - 7)
+
+
+def conv_violations(gpu, ref, mag, rel=2e-3, ulp=None):
+    """Indices where the conv bound fails, and the worst ratio err / bound.
+
+    Bound: rel * S + one ulp of the output format at ref (fp16 unless ulp is given).
+    """
     g = np.asarray(gpu, dtype=np.float64)
     err = np.abs(g - ref)
-    bound = 2e-3 * mag + ulp16(ref)
+    bound = rel * mag + (ulp16(ref) if ulp is None else ulp(ref))
     bad = ~(err <= bound)  # NaN counts as a failure
     ratio = float(np.max(err / bound)) if err.size else 0.0
     return np.flatnonzero(bad.reshape(-1)), ratio
 
 
-def assert_conv_close(gpu, ref, mag, what=""):
-    bad, ratio = conv_violations(gpu, ref, mag)
+def assert_conv_close(gpu, ref, mag, what="", rel=2e-3, ulp=None):
+    bad, ratio = conv_violations(gpu, ref, mag, rel, ulp)
     if bad.size:
         g = np.asarray(gpu, dtype=np.float64).reshape(-1)
         i = bad[0]
@@ -157,10 +186,11 @@ def assert_conv_close(gpu, ref, mag, what=""):
     return ratio
 
 
-def assert_gn_close(gpu, ref, what=""):
+def assert_gn_close(gpu, ref, what="", ulp=None):
+    """|gpu - ref| <= 1e-3 |ref| + 2^-14, plus one output ulp at ref when ulp is given (bf16)."""
     g = np.asarray(gpu, dtype=np.float64)
     err = np.abs(g - ref)
-    bound = 1e-3 * np.abs(ref) + 2.0 ** -14
+    bound = 1e-3 * np.abs(ref) + 2.0 ** -14 + (0.0 if ulp is None else ulp(ref))
     bad = ~(err <= bound)
     if np.any(bad):
         i = np.flatnonzero(bad.reshape(-1))[0]

@@ -213,3 +213,11 @@ def test_calibration_without_a_device_reports_no_device():
     need = c3d.conv3d_calibrate_scratch_bytes()
     assert lib.conv3d_calibrate_mfma(A, need, ctypes.byref(d1), ctypes.byref(d2), None) == \
         c3d.CONV3D_ERR_NO_DEVICE
+
+
+def test_bf16_flag_plans_every_path():
+    for d in (desc(flags=c3d.CONV3D_F_BF16 | c3d.CONV3D_F_BIAS), desc(t=1, flags=c3d.CONV3D_F_BF16),
+              desc(kt=1, kh=1, kw=1, pad_t_front=0, pad_h=0, pad_w=0, flags=c3d.CONV3D_F_BF16)):
+        p = c3d.conv3d_plan(d)
+        assert p.info().flops > 0
+    assert plan_status(desc(flags=16)) == c3d.CONV3D_ERR_INVALID_ARG

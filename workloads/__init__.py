@@ -119,9 +119,32 @@ def _fill_chunks(flat, ss, draw):
             list(ex.map(one, range(nchunks)))
 
 
-def normal_f16(ss, shape, mean=0.0, std=1.0, channel_scale=None):
-    """N(mean, std) drawn as float32, optionally scaled per channel (last axis), rounded once to fp16."""
-    out = np.empty(shape, np.float16)
+def to_bf16(a):
+    """float32 values -> bf16 storage (uint16 bits), rounded once to nearest even.
+
+    Finite inputs only (the generators here draw finite values).  bf16 is the
+    upper half of an IEEE binary32, so rounding adds half an ulp of the kept
+    part (one less on an even tie) before truncating the lower 16 bits.
+    """
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    return ((b + (np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
+
+
+def _store(v, dtype):
+    """float32 draws -> the storage of dtype ("f16": float16, "bf16": uint16 bits)."""
+    return to_bf16(v) if dtype == "bf16" else v.astype(np.float16)
+
+
+def _storage(dtype):
+    return np.uint16 if dtype == "bf16" else np.float16
+
+
+def normal_f16(ss, shape, mean=0.0, std=1.0, channel_scale=None, dtype="f16"):
+    """N(mean, std) drawn as float32, optionally scaled per channel (last axis), rounded once to fp16.
+
+    dtype="bf16" rounds the same draws to bf16 instead (uint16 bits).
+    """
+    out = np.empty(shape, _storage(dtype))
     flat = out.reshape(-1)
     c = shape[-1]
 
@@ -134,7 +157,7 @@ def normal_f16(ss, shape, mean=0.0, std=1.0, channel_scale=None):
         if channel_scale is not None:
             # chunk starts are multiples of CHUNK, itself a multiple of c (c divides 2^24 here)
             v.reshape(-1, c)[:, channel_scale[0]] *= np.float32(channel_scale[1])
-        return v.astype(np.float16)
+        return _store(v, dtype)
 
     if channel_scale is not None and CHUNK % c:
         raise ValueError("channel count must divide the chunk size")
@@ -142,13 +165,16 @@ def normal_f16(ss, shape, mean=0.0, std=1.0, channel_scale=None):
     return out
 
 
-def uniform_f16(ss, shape, bound):
-    return _gen(ss).uniform(-bound, bound, size=shape).astype(np.float16)
+def uniform_f16(ss, shape, bound, dtype="f16"):
+    return _store(_gen(ss).uniform(-bound, bound, size=shape).astype(np.float32), dtype)
 
 
 def conv_inputs(shape: ConvShape, seed: int, w_bound=None, b_std=0.02, with_bias=True,
-                hot_channels=0, hot_scale=50.0):
-    """x, w, b (fp16 numpy) for one conv.  ``hot_channels`` input channels x hot_scale."""
+                hot_channels=0, hot_scale=50.0, dtype="f16"):
+    """x, w, b (fp16 numpy; bf16 bits as uint16 with dtype="bf16") for one conv.
+
+    ``hot_channels`` input channels are scaled by hot_scale.
+    """
     sx, sw, sb, sp = _seeds(seed, 4)
     if w_bound is None:
         w_bound = kaiming_bound(shape)
@@ -156,9 +182,9 @@ def conv_inputs(shape: ConvShape, seed: int, w_bound=None, b_std=0.02, with_bias
     if hot_channels:
         hot = np.sort(_gen(sp).permutation(shape.cin)[:hot_channels])
         scale = (hot, hot_scale)
-    x = normal_f16(sx, shape.x_shape, channel_scale=scale)
-    w = uniform_f16(sw, shape.w_shape, w_bound)
-    b = normal_f16(sb, (shape.cout,), 0.0, b_std) if with_bias else None
+    x = normal_f16(sx, shape.x_shape, channel_scale=scale, dtype=dtype)
+    w = uniform_f16(sw, shape.w_shape, w_bound, dtype)
+    b = normal_f16(sb, (shape.cout,), 0.0, b_std, dtype=dtype) if with_bias else None
     return {"x": x, "w": w, "b": b}
 
 
@@ -182,29 +208,30 @@ def workload_inputs(k: int):
     raise KeyError(k)
 
 
-def block_inputs(shape: ConvShape, seed: int):
+def block_inputs(shape: ConvShape, seed: int, dtype="f16"):
     """Decoder-block tensors in the order x, gamma1, beta1, w1, b1, gamma2, beta2, w2, b2."""
     r = _seeds(seed, 9)
     c = shape.cin
     bound = kaiming_bound(shape)
     return {
         "shape": shape,
-        "x": normal_f16(r[0], shape.x_shape),
-        "gamma1": normal_f16(r[1], (c,), 1.0, 0.1),
-        "beta1": normal_f16(r[2], (c,), 0.0, 0.1),
-        "w1": uniform_f16(r[3], shape.w_shape, bound),
-        "b1": normal_f16(r[4], (shape.cout,), 0.0, 0.02),
-        "gamma2": normal_f16(r[5], (c,), 1.0, 0.1),
-        "beta2": normal_f16(r[6], (c,), 0.0, 0.1),
-        "w2": uniform_f16(r[7], shape.w_shape, bound),
-        "b2": normal_f16(r[8], (shape.cout,), 0.0, 0.02),
+        "x": normal_f16(r[0], shape.x_shape, dtype=dtype),
+        "gamma1": normal_f16(r[1], (c,), 1.0, 0.1, dtype=dtype),
+        "beta1": normal_f16(r[2], (c,), 0.0, 0.1, dtype=dtype),
+        "w1": uniform_f16(r[3], shape.w_shape, bound, dtype),
+        "b1": normal_f16(r[4], (shape.cout,), 0.0, 0.02, dtype=dtype),
+        "gamma2": normal_f16(r[5], (c,), 1.0, 0.1, dtype=dtype),
+        "beta2": normal_f16(r[6], (c,), 0.0, 0.1, dtype=dtype),
+        "w2": uniform_f16(r[7], shape.w_shape, bound, dtype),
+        "b2": normal_f16(r[8], (shape.cout,), 0.0, 0.02, dtype=dtype),
         "groups": BLOCK_GROUPS,
         "eps": BLOCK_EPS,
     }
 
 
-def gn_inputs(n: int, thw_shape, c: int, seed: int, mean=0.0, std=1.0):
-    """x [n, *thw_shape, c] ~ N(mean, std), gamma ~ N(1, 0.1), beta ~ N(0, 0.1), all fp16."""
+def gn_inputs(n: int, thw_shape, c: int, seed: int, mean=0.0, std=1.0, dtype="f16"):
+    """x [n, *thw_shape, c] ~ N(mean, std), gamma ~ N(1, 0.1), beta ~ N(0, 0.1), all fp16 (or bf16)."""
     sx, sg, sb = _seeds(seed, 3)
-    x = normal_f16(sx, (n,) + tuple(thw_shape) + (c,), mean, std)
-    return {"x": x, "gamma": normal_f16(sg, (c,), 1.0, 0.1), "beta": normal_f16(sb, (c,), 0.0, 0.1)}
+    x = normal_f16(sx, (n,) + tuple(thw_shape) + (c,), mean, std, dtype=dtype)
+    return {"x": x, "gamma": normal_f16(sg, (c,), 1.0, 0.1, dtype=dtype),
+            "beta": normal_f16(sb, (c,), 0.0, 0.1, dtype=dtype)}
