@@ -29,12 +29,14 @@ CONV3D_F_BIAS = 1
 CONV3D_F_RESIDUAL = 2
 CONV3D_F_NO_T1_FASTPATH = 4
 CONV3D_F_BF16 = 8
+CONV3D_F_CHUNK = 16
 
 CONV3D_PATH_GENERAL = 0
 CONV3D_PATH_T1_FOLD = 1
 CONV3D_PATH_POINTWISE = 2
 
 EXPORTED = ("conv3d_plan", "conv3d_plan_query", "conv3d_plan_destroy", "conv3d_forward",
+            "conv3d_forward_chunk",
             "groupnorm_silu_workspace", "groupnorm_silu", "groupnorm_silu_bf16",
             "conv3d_calibrate_scratch_bytes",
             "conv3d_calibrate_mfma", "conv3d_calibrate_hbm", "conv3d_status_str",
@@ -89,6 +91,8 @@ def load_library(path: str = LIB_PATH):
     lib.conv3d_plan_destroy.argtypes = [vp]
     lib.conv3d_plan_destroy.restype = None
     lib.conv3d_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.conv3d_forward_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.conv3d_forward_chunk.restype = ctypes.c_int
     lib.conv3d_forward.restype = ctypes.c_int
     lib.groupnorm_silu_workspace.argtypes = [i32, i64, i32, i32]
     lib.groupnorm_silu_workspace.restype = sz
@@ -191,6 +195,16 @@ def conv3d_forward(plan: Plan, x, weight, bias, residual, y, workspace=None, wor
     _check(load_library().conv3d_forward(plan.handle, _addr(x), _addr(weight), _addr(bias),
                                          _addr(residual), _addr(y), _addr(workspace),
                                          workspace_bytes, _stream(stream)))
+
+
+def conv3d_forward_chunk(plan: Plan, x_prev, x, weight, bias, residual, y, workspace,
+                         workspace_bytes=None, stream=None) -> None:
+    """Enqueue one chunk of a chunked causal decode (plan made with CONV3D_F_CHUNK)."""
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().conv3d_forward_chunk(plan.handle, _addr(x_prev), _addr(x), _addr(weight),
+                                               _addr(bias), _addr(residual), _addr(y), _addr(workspace),
+                                               workspace_bytes, _stream(stream)))
 
 
 def groupnorm_silu_workspace(n, thw, c, groups) -> int:

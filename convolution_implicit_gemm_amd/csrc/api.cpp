@@ -125,7 +125,21 @@ struct conv3d_plan_s {
     size_t ws_bytes;
     int64_t x_elems, w_elems, y_elems;
     double flops;
+    // chunked causal decoding (CONV3D_F_CHUNK): per sample, a head conv over
+    // [x_prev; the first frames of x] copied into the workspace gives the
+    // first head_out output frames, and a conv over x without temporal padding
+    // (main, absent when x is too short) gives the rest
+    bool chunk = false;
+    conv3d_plan_s *head = nullptr, *main = nullptr;
+    int head_t = 0, head_out = 0;
+    size_t head_in_bytes = 0;  // 256-aligned; the sub-plans' workspace follows
+    ~conv3d_plan_s() {
+        delete head;
+        delete main;
+    }
 };
+
+static conv3d_status plan_chunk(const conv3d_desc *d, conv3d_plan_t *out, size_t *workspace_bytes);
 
 extern "C" {
 
@@ -158,8 +172,10 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
         return fail(CONV3D_ERR_INVALID_ARG, "padding must be smaller than the kernel extent");
     if (d->t_pad_mode != CONV3D_TPAD_ZERO && d->t_pad_mode != CONV3D_TPAD_REPLICATE)
         return fail(CONV3D_ERR_INVALID_ARG, "unknown t_pad_mode %d", d->t_pad_mode);
-    const uint32_t known = CONV3D_F_BIAS | CONV3D_F_RESIDUAL | CONV3D_F_NO_T1_FASTPATH | CONV3D_F_BF16;
+    const uint32_t known =
+        CONV3D_F_BIAS | CONV3D_F_RESIDUAL | CONV3D_F_NO_T1_FASTPATH | CONV3D_F_BF16 | CONV3D_F_CHUNK;
     if (d->flags & ~known) return fail(CONV3D_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags & ~known);
+    if (d->flags & CONV3D_F_CHUNK) return plan_chunk(d, out, workspace_bytes);
     const int To = d->t + d->pad_t_front + d->pad_t_back - d->kt + 1;
     const int Ho = d->h + 2 * d->pad_h - d->kh + 1;
     const int Wo = d->w + 2 * d->pad_w - d->kw + 1;
@@ -285,6 +301,15 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
 conv3d_status conv3d_plan_query(conv3d_plan_t p, conv3d_plan_info *info) {
     if (!p || !info) return fail(CONV3D_ERR_INVALID_ARG, "null argument");
     memset(info, 0, sizeof(*info));
+    if (p->chunk) {  // the main conv's kernel, with the whole chunk's GEMM and work
+        const conv3d_status st = conv3d_plan_query(p->main ? p->main : p->head, info);
+        if (st != CONV3D_OK) return st;
+        info->t_out = p->d.t;
+        info->gemm_m = (int64_t)p->d.n * p->d.t * info->h_out * info->w_out;
+        info->flops = p->flops;
+        info->workspace_bytes = p->ws_bytes;
+        return ok();
+    }
     info->path = p->path;
     info->t_out = p->prm.To;
     info->h_out = p->prm.Ho;
@@ -324,6 +349,7 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
                              const void *residual, void *y, void *workspace, size_t workspace_bytes,
                              void *stream) {
     if (!p) return fail(CONV3D_ERR_INVALID_ARG, "null plan");
+    if (p->chunk) return fail(CONV3D_ERR_INVALID_ARG, "a CONV3D_F_CHUNK plan runs through conv3d_forward_chunk");
     const bool has_bias = p->d.flags & CONV3D_F_BIAS, has_res = p->d.flags & CONV3D_F_RESIDUAL;
     if (!x || !weight || !y) return fail(CONV3D_ERR_INVALID_ARG, "x, weight and y are required");
     if (has_bias && !bias) return fail(CONV3D_ERR_INVALID_ARG, "plan has CONV3D_F_BIAS but bias is null");
@@ -382,6 +408,62 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
     if (q.sk_tiles) {
         e = p->tile->launch_fixup(q, s);
         if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "fixup launch: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
+conv3d_status conv3d_forward_chunk(conv3d_plan_t p, const void *x_prev, const void *x, const void *weight,
+                                   const void *bias, const void *residual, void *y, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    if (!p) return fail(CONV3D_ERR_INVALID_ARG, "null plan");
+    if (!p->chunk) return fail(CONV3D_ERR_INVALID_ARG, "conv3d_forward_chunk needs a plan made with CONV3D_F_CHUNK");
+    const bool has_bias = p->d.flags & CONV3D_F_BIAS, has_res = p->d.flags & CONV3D_F_RESIDUAL;
+    if (!x_prev || !x || !weight || !y) return fail(CONV3D_ERR_INVALID_ARG, "x_prev, x, weight and y are required");
+    if (has_bias && !bias) return fail(CONV3D_ERR_INVALID_ARG, "plan has CONV3D_F_BIAS but bias is null");
+    if (has_res && !residual) return fail(CONV3D_ERR_INVALID_ARG, "plan has CONV3D_F_RESIDUAL but residual is null");
+    if (misaligned(x_prev) || misaligned(x) || misaligned(weight) || misaligned(y) || (has_bias && misaligned(bias)) ||
+        (has_res && misaligned(residual)) || (workspace && misaligned(workspace)))
+        return fail(CONV3D_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    const conv3d_desc &d = p->d;
+    const size_t frame_in = (size_t)d.h * d.w * d.c_in * 2;
+    const int64_t hw_out = (int64_t)(d.h + 2 * d.pad_h - d.kh + 1) * (d.w + 2 * d.pad_w - d.kw + 1);
+    const size_t frame_out = (size_t)hw_out * d.c_out * 2;
+    const size_t xb = frame_in * d.t * d.n, pb = frame_in * d.pad_t_front * d.n, yb = frame_out * d.t * d.n;
+    if (overlap(y, yb, x, xb) || overlap(y, yb, x_prev, pb) || overlap(y, yb, weight, (size_t)p->w_elems * 2) ||
+        (has_bias && overlap(y, yb, bias, (size_t)d.c_out * 2)) || (has_res && overlap(y, yb, residual, yb)))
+        return fail(CONV3D_ERR_INVALID_ARG, "y overlaps an input");
+    if (!workspace || workspace_bytes < p->ws_bytes)
+        return fail(CONV3D_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p->ws_bytes,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (overlap(workspace, p->ws_bytes, y, yb) || overlap(workspace, p->ws_bytes, x, xb) ||
+        overlap(workspace, p->ws_bytes, x_prev, pb) || overlap(workspace, p->ws_bytes, weight, (size_t)p->w_elems * 2) ||
+        (has_res && overlap(workspace, p->ws_bytes, residual, yb)))
+        return fail(CONV3D_ERR_INVALID_ARG, "workspace overlaps a tensor");
+    conv3d_status st = check_device();
+    if (st != CONV3D_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *hin = static_cast<char *>(workspace);
+    char *sub_ws = hin + p->head_in_bytes;
+    const size_t sub_bytes = p->ws_bytes - p->head_in_bytes;
+    const int ptf = d.pad_t_front;
+    for (int n = 0; n < d.n; ++n) {
+        const char *xp_n = static_cast<const char *>(x_prev) + frame_in * ptf * n;
+        const char *x_n = static_cast<const char *>(x) + frame_in * d.t * n;
+        char *y_n = static_cast<char *>(y) + frame_out * d.t * n;
+        const char *r_n = has_res ? static_cast<const char *>(residual) + frame_out * d.t * n : nullptr;
+        // head input: the history, then the first frames of this chunk
+        hipError_t e = hipMemcpyAsync(hin, xp_n, frame_in * ptf, hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(hin + frame_in * ptf, x_n, frame_in * (p->head_t - ptf), hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "chunk head copy: %s", hipGetErrorString(e));
+        st = conv3d_forward(p->head, hin, weight, bias, r_n, y_n, sub_ws, sub_bytes, stream);
+        if (st != CONV3D_OK) return st;
+        if (p->main) {
+            const size_t off = frame_out * p->head_out;
+            st = conv3d_forward(p->main, x_n, weight, bias, r_n ? r_n + off : nullptr, y_n + off, sub_ws, sub_bytes,
+                                stream);
+            if (st != CONV3D_OK) return st;
+        }
     }
     return ok();
 }
@@ -461,5 +543,60 @@ conv3d_status conv3d_calibrate_hbm(const void *src, void *dst, size_t bytes, dou
     if (st != CONV3D_OK) return st;
     hipError_t e = c3d::calibrate_hbm(src, dst, bytes, static_cast<hipStream_t>(stream), read_gbs, copy_gbs);
     if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "hbm calibration: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// CONV3D_F_CHUNK: output frame t of a chunk reads frames t-kt+1 .. t, the
+// negative ones from x_prev (the previous chunk's last kt-1 frames).  Output
+// frames 0 .. min(T, kt-1)-1 come from a head conv over [x_prev; x frames
+// 0 .. min(T, kt-1)-1] and the rest from the chunk alone; both without
+// temporal padding, one sample at a time (the sub-convs' outputs are frame
+// ranges of each sample).
+static conv3d_status plan_chunk(const conv3d_desc *d, conv3d_plan_t *out, size_t *workspace_bytes) {
+    if (d->kt < 2 || d->pad_t_front != d->kt - 1 || d->pad_t_back != 0)
+        return fail(CONV3D_ERR_INVALID_ARG, "CONV3D_F_CHUNK needs kt > 1, pad_t_front = kt-1 and pad_t_back = 0");
+    conv3d_desc full = *d;  // the same conv with causal padding: validates every extent and limit
+    full.flags &= ~(uint32_t)CONV3D_F_CHUNK;
+    conv3d_plan_t shadow = nullptr;
+    size_t ws = 0;
+    conv3d_status st = conv3d_plan(&full, &shadow, &ws);
+    if (st != CONV3D_OK) return st;
+    conv3d_plan_s *p = new (std::nothrow) conv3d_plan_s();
+    if (!p) {
+        conv3d_plan_destroy(shadow);
+        return fail(CONV3D_ERR_INVALID_ARG, "out of host memory");
+    }
+    p->d = *d;
+    p->chunk = true;
+    p->x_elems = shadow->x_elems;
+    p->w_elems = shadow->w_elems;
+    p->y_elems = shadow->y_elems;
+    conv3d_plan_destroy(shadow);
+    const int hist = d->kt - 1;
+    p->head_out = d->t < hist ? d->t : hist;
+    p->head_t = hist + p->head_out;
+    conv3d_desc sub = *d;
+    sub.flags = d->flags & (CONV3D_F_BIAS | CONV3D_F_RESIDUAL | CONV3D_F_BF16 | CONV3D_F_NO_T1_FASTPATH);
+    sub.n = 1;
+    sub.pad_t_front = 0;
+    sub.pad_t_back = 0;
+    sub.t_pad_mode = CONV3D_TPAD_ZERO;
+    sub.t = p->head_t;
+    size_t ws_head = 0, ws_main = 0;
+    st = conv3d_plan(&sub, &p->head, &ws_head);
+    if (st == CONV3D_OK && d->t > hist) {
+        sub.t = d->t;
+        st = conv3d_plan(&sub, &p->main, &ws_main);
+    }
+    if (st != CONV3D_OK) {
+        delete p;
+        return st;
+    }
+    p->head_in_bytes = ((size_t)p->head_t * d->h * d->w * d->c_in * 2 + 255) & ~(size_t)255;
+    p->ws_bytes = p->head_in_bytes + (ws_head > ws_main ? ws_head : ws_main);
+    p->flops = (double)d->n * (p->head->flops + (p->main ? p->main->flops : 0.0));
+    p->path = CONV3D_PATH_GENERAL;
+    *out = p;
+    *workspace_bytes = p->ws_bytes;
     return ok();
 }

@@ -58,7 +58,8 @@ enum {
     CONV3D_F_BIAS = 1u,            /* add bias[Cout] */
     CONV3D_F_RESIDUAL = 2u,        /* add residual[N,To,Ho,Wo,Cout] (fp32 add, one rounding) */
     CONV3D_F_NO_T1_FASTPATH = 4u,  /* never fold temporal taps, even when it is exact */
-    CONV3D_F_BF16 = 8u             /* x, weight, bias, residual and y are bf16, not fp16 */
+    CONV3D_F_BF16 = 8u,            /* x, weight, bias, residual and y are bf16, not fp16 */
+    CONV3D_F_CHUNK = 16u           /* chunked causal decoding: see conv3d_forward_chunk */
 };
 
 /* Execution paths a plan may choose. */
@@ -147,6 +148,28 @@ void conv3d_plan_destroy(conv3d_plan_t p);
 conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight, const void *bias,
                              const void *residual, void *y, void *workspace,
                              size_t workspace_bytes, void *stream);
+
+/*
+ * Chunked causal decoding: a long video decoded T frames at a time, where
+ * each chunk's history is the previous chunk's last kt-1 input frames instead
+ * of the replicated (or zero) front padding.  The plan must be made with
+ * CONV3D_F_CHUNK, pad_t_front = kt-1 > 0 and pad_t_back = 0 (else
+ * INVALID_ARG); t_pad_mode is then unused.
+ *   x_prev: [n][kt-1][h][w][c_in]   the previous chunk's last frames
+ *   x:      [n][t][h][w][c_in]      this chunk
+ *   y (and residual): [n][t][h_out][w_out][c_out]
+ * y equals the conv of [x_prev; x] along t with no temporal padding.  Decoding
+ * a video chunk by chunk (the first chunk with the ordinary causal plan, the
+ * next ones with x_prev = the last kt-1 frames of the previous chunk's input)
+ * therefore gives the same outputs as decoding it whole.  Per sample it copies
+ * x_prev and the first min(t, kt-1) frames of x into the workspace and runs two
+ * convs (the plan's workspace covers both).  A CONV3D_F_CHUNK plan is rejected
+ * by conv3d_forward and vice versa.  Errors as conv3d_forward, plus
+ * INVALID_ARG for a null x_prev or y overlapping it.
+ */
+conv3d_status conv3d_forward_chunk(conv3d_plan_t p, const void *x_prev, const void *x, const void *weight,
+                                   const void *bias, const void *residual, void *y, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /*
  * GroupNorm + optional SiLU over channels-last fp16 data.

@@ -220,4 +220,37 @@ def test_bf16_flag_plans_every_path():
               desc(kt=1, kh=1, kw=1, pad_t_front=0, pad_h=0, pad_w=0, flags=c3d.CONV3D_F_BF16)):
         p = c3d.conv3d_plan(d)
         assert p.info().flops > 0
-    assert plan_status(desc(flags=16)) == c3d.CONV3D_ERR_INVALID_ARG
+    assert plan_status(desc(flags=32)) == c3d.CONV3D_ERR_INVALID_ARG
+
+
+def test_chunk_plans_and_argument_checks():
+    lib = c3d.load_library()
+    ch = c3d.CONV3D_F_CHUNK | c3d.CONV3D_F_BIAS
+    # only causal shapes chunk: pad_t_front = kt-1, no back padding
+    assert plan_status(desc(flags=ch, pad_t_front=1, pad_t_back=1)) == c3d.CONV3D_ERR_INVALID_ARG
+    assert plan_status(desc(flags=ch, kt=1, pad_t_front=0)) == c3d.CONV3D_ERR_INVALID_ARG
+    p = c3d.conv3d_plan(desc(flags=ch))
+    info = p.info()
+    assert p.workspace_bytes > 0 and info.t_out == desc().t and info.flops > 0
+    short = c3d.conv3d_plan(desc(flags=ch, t=1))       # shorter than the history: head conv only
+    assert short.info().t_out == 1 and short.workspace_bytes > 0
+    # a chunk plan runs only through conv3d_forward_chunk, and the other way round
+    assert lib.conv3d_forward(p.handle, A, A + 64 * MB, A + 128 * MB, None, A + 256 * MB, A + 512 * MB,
+                              p.workspace_bytes, None) == c3d.CONV3D_ERR_INVALID_ARG
+    plain = c3d.conv3d_plan(desc())
+
+    def fc(plan, xp=A + 768 * MB, x=A, ws=A + 512 * MB, wsb=None):
+        return lib.conv3d_forward_chunk(plan.handle, xp, x, A + 128 * MB, A + 192 * MB, None, A + 256 * MB, ws,
+                                        plan.workspace_bytes if wsb is None else wsb, None)
+    assert fc(plain) == c3d.CONV3D_ERR_INVALID_ARG
+    assert fc(p, xp=None) == c3d.CONV3D_ERR_INVALID_ARG
+    assert fc(p, xp=A + 256 * MB + 64) == c3d.CONV3D_ERR_INVALID_ARG   # y overlaps x_prev
+    assert fc(p, wsb=16) == c3d.CONV3D_ERR_WORKSPACE
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="host without a GPU only")
+def test_chunk_without_a_device_reports_no_device():
+    lib = c3d.load_library()
+    p = c3d.conv3d_plan(desc(flags=c3d.CONV3D_F_CHUNK | c3d.CONV3D_F_BIAS))
+    assert lib.conv3d_forward_chunk(p.handle, A + 768 * MB, A, A + 128 * MB, A + 192 * MB, None, A + 256 * MB,
+                                    A + 512 * MB, p.workspace_bytes, None) == c3d.CONV3D_ERR_NO_DEVICE
