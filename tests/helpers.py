@@ -97,7 +97,7 @@ def forced_tile(name):
 def tile_names():
     """Tile configurations compiled into the library (by forcing each name in turn)."""
     names = ["m256n256k64s2w4", "m256n256k32s4w4", "m256n256k64s2w8", "m256n256k64s2a3w8",
-             "m256n256k64s2a3w4", "m256n128k64s2w4", "m128n128k64s3w4", "m128n64k64s2w4",
+             "m256n256k64s2a3w4", "m256n128k64s2a3w4", "m128n128k64s2a3w4", "m128n64k64s2w4",
              "m128n32k32s2w4"]
     return names
 

@@ -121,21 +121,27 @@ def test_k_split_switch():
         assert i.split_tiles == 0 and i.split_pieces == 0
     finally:
         del os.environ["CONV3D_STREAMK"]
+    # splitting applies to tiles that hold a CU alone (one workgroup per CU)
     os.environ["CONV3D_STREAMK"] = "1"
+    os.environ["CONV3D_TILE"] = "m256n256k64s2a3w8"
     try:
         p = c3d.conv3d_plan(desc(t=3, h=10, w=13, c_in=64, c_out=72))
         i = p.info()
         assert i.split_tiles > 0 and i.split_pieces >= 2
         assert p.workspace_bytes >= i.split_tiles * i.split_pieces * i.tile_m * i.tile_n * 4
+        os.environ["CONV3D_TILE"] = "m128n128k64s2a3w4"
+        i = c3d.conv3d_plan(desc(t=3, h=10, w=13, c_in=64, c_out=72)).info()
+        assert i.split_tiles == 0
     finally:
         del os.environ["CONV3D_STREAMK"]
+        del os.environ["CONV3D_TILE"]
 
 
 def test_forced_tile_and_unknown_tile():
-    os.environ["CONV3D_TILE"] = "m128n128k64s3w4"
+    os.environ["CONV3D_TILE"] = "m128n128k64s2a3w4"
     try:
         i = c3d.conv3d_plan(desc()).info()
-        assert (i.tile_m, i.tile_n, i.tile_k, i.stages) == (128, 128, 64, 3)
+        assert (i.tile_m, i.tile_n, i.tile_k, i.stages) == (128, 128, 64, 2)
         os.environ["CONV3D_TILE"] = "no-such-tile"
         assert plan_status(desc()) == c3d.CONV3D_ERR_INVALID_ARG
     finally:
