@@ -275,7 +275,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
         const int m_last = (m0 + BM < M ? m0 + BM : M) - 1;
         lo = vb_of(m0, t_, h_, w_) - (p.ptf * HW + p.ph * W + p.pw);
         lo = lo < 0 ? 0 : lo;
-        hi = vb_of(m_last, t_, h_, w_) + (p.kt - 1) * HW + (p.kh - 1) * W + (p.kw - 1) + 1;
+        // the last row's farthest tap; a clamped (replicated) frame lies inside
+        hi = vb_of(m_last, t_, h_, w_) + (p.kt - 1 - p.ptf) * HW + (p.kh - 1 - p.ph) * W + (p.kw - 1 - p.pw) + 1;
         hi = hi > p.in_vox ? p.in_vox : hi;
         if (hi < lo) hi = lo;
     }
@@ -654,8 +655,8 @@ int64_t tile_window_voxels(const ConvParams &q, int bm) {
     const int64_t HW = (int64_t)q.H * q.W;
     const int64_t skip = rows * (q.W > q.Wo ? q.W - q.Wo : 0) + frames * (q.H > q.Ho ? q.H - q.Ho : 0) * q.W +
                          samples * (q.T > q.To ? q.T - q.To : 0) * HW;
-    const int64_t halo = (int64_t)q.ptf * HW + (int64_t)q.ph * q.W + q.pw + (int64_t)(q.kt - 1) * HW +
-                         (int64_t)(q.kh - 1) * q.W + (q.kw - 1) + 1;
+    // taps reach from (-ptf, -ph, -pw) to (kt-1-ptf, kh-1-ph, kw-1-pw) around a row
+    const int64_t halo = (int64_t)(q.kt - 1) * HW + (int64_t)(q.kh - 1) * q.W + (q.kw - 1) + 1;
     return (bm - 1) + skip + halo;
 }
 

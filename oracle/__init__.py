@@ -21,6 +21,9 @@ Function inventory and pins (tests/test_oracle_*.py):
   groupnorm_silu    -- pinned: torch.nn.functional.group_norm (fp64, CPU) +
                        SiLU; closed forms (constant group, +-a halves);
                        per-sample independence; shift/scale invariance.
+  groupnorm_silu_points -- pinned: equals groupnorm_silu (values and
+                       statistics) at every element of small tensors, fp16
+                       and fp64 inputs.
   bf16_to_f64       -- pinned: every one of the 65,536 patterns against the
                        value sign * 2^(e-127) * (1 + f/128) (normal) or
                        sign * 2^-126 * f/128 (subnormal) built term by term.
@@ -74,6 +77,10 @@ def _load():
         lib.oracle_groupnorm_silu.argtypes = [d, i, ctypes.c_int64, i, i, d, d, ctypes.c_double,
                                               i, d, d, d]
         lib.oracle_groupnorm_silu.restype = i
+        lib.oracle_groupnorm_silu_points.argtypes = [vp, i, i, ctypes.c_int64, i, i, d, d, ctypes.c_double, i,
+                                                     ctypes.POINTER(ctypes.c_int64),
+                                                     ctypes.POINTER(ctypes.c_int32), ctypes.c_int64, d, d, d]
+        lib.oracle_groupnorm_silu_points.restype = i
         lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_f64.restype = ctypes.c_double
         lib.oracle_num_threads.argtypes = []
@@ -204,6 +211,33 @@ def groupnorm_silu(x, gamma, beta, groups, eps=1e-6, apply_silu=True, return_sta
     if return_stats:
         return y, mean, var
     return y
+
+
+def groupnorm_silu_points(x, gamma, beta, groups, vox_idx, ch_idx, eps=1e-6, apply_silu=True):
+    """GroupNorm (+SiLU) at selected elements: flat voxel vox_idx[i] (over N*THW), channel ch_idx[i].
+
+    x: [N, ..., C]; a float16 array is read in place and widened exactly in C,
+    so that multi-GB activations need no fp64 copy.  The statistics are the
+    two-pass ones of groupnorm_silu.  Returns (y[i], mean[N, groups], var[N, groups]).
+    """
+    xp, xh, xkeep = _maybe_f16(x)
+    shape = xkeep.shape
+    n, c = shape[0], shape[-1]
+    thw = int(np.prod(shape[1:-1])) if len(shape) > 2 else 1
+    g, bt = _f64(gamma), _f64(beta)
+    vox_idx = np.ascontiguousarray(vox_idx, dtype=np.int64)
+    ch_idx = np.ascontiguousarray(ch_idx, dtype=np.int32)
+    y = np.empty(vox_idx.shape[0], np.float64)
+    mean = np.empty((n, groups), np.float64)
+    var = np.empty((n, groups), np.float64)
+    rc = _load().oracle_groupnorm_silu_points(
+        xp, xh, n, thw, c, groups, _ptr(g), _ptr(bt), float(eps), 1 if apply_silu else 0,
+        vox_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        ch_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), vox_idx.shape[0], _ptr(y), _ptr(mean), _ptr(var))
+    del xkeep
+    if rc != 0:
+        raise ValueError("oracle_groupnorm_silu_points rejected the input")
+    return y, mean, var
 
 
 def decoder_block(x, gn1, conv1, gn2, conv2, groups=32, eps=1e-6, pads=(2, 0, 1, 1),

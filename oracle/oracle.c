@@ -29,6 +29,8 @@
  *    variance as the mean of squared deviations, then
  *    yhat = (x - mean) / sqrt(var + eps) * gamma_c + beta_c and
  *    out = yhat / (1 + exp(-yhat)).  Groups are contiguous channel ranges.
+ *    groupnorm_silu_points evaluates the same definition at selected elements
+ *    of tensors too large to widen to fp64 whole.
  *
  * Parity pins for every function here live in tests/test_oracle_*.py.
  */
@@ -229,6 +231,73 @@ int oracle_groupnorm_silu(const double *x, int N, int64_t thw, int C, int groups
             }
         if (mean_out) mean_out[i] = mean;
         if (var_out) var_out[i] = var;
+    }
+    return 0;
+}
+
+/*
+ * GroupNorm (+ optional SiLU) at selected elements of a large tensor, with
+ * the same two-pass statistics as oracle_groupnorm_silu.  x: [N][THW][C],
+ * fp16 bit patterns when x_f16 is set (widened exactly on the fly, so a
+ * multi-GB activation needs no fp64 copy), doubles otherwise.  Element i is
+ * voxel vox[i] (flat over N*THW) at channel ch[i].  Each pass sums a fixed
+ * partition of the voxels into 64 ranges and adds the range sums in order,
+ * so the result does not depend on the thread count.  Writes y[i] and, per
+ * (sample, group), mean_out / var_out (biased variance).
+ */
+static double gn_elem(const void *x, int x_f16, size_t i) {
+    return x_f16 ? oracle_f16_to_f64(((const uint16_t *)x)[i]) : ((const double *)x)[i];
+}
+
+int oracle_groupnorm_silu_points(const void *x, int x_f16, int N, int64_t thw, int C, int groups,
+                                 const double *gamma, const double *beta, double eps, int apply_silu,
+                                 const int64_t *vox, const int32_t *ch, int64_t npts, double *y,
+                                 double *mean_out, double *var_out) {
+    enum { NB = 64 };
+    if (N < 1 || thw < 1 || C < 1 || groups < 1 || C % groups != 0) return -1;
+    for (int64_t i = 0; i < npts; ++i)
+        if (vox[i] < 0 || vox[i] >= (int64_t)N * thw || ch[i] < 0 || ch[i] >= C) return -1;
+    int cg = C / groups;
+    double cnt = (double)thw * cg;
+    double *part = (double *)calloc((size_t)NB * groups, sizeof(double));
+    if (!part) return -1;
+    for (int n = 0; n < N; ++n) {
+        size_t base = (size_t)n * thw * C;
+        double *mean = mean_out + (size_t)n * groups, *var = var_out + (size_t)n * groups;
+        for (int pass = 0; pass < 2; ++pass) {
+#pragma omp parallel for schedule(dynamic, 1)
+            for (int b = 0; b < NB; ++b) {
+                int64_t v0 = thw * b / NB, v1 = thw * (b + 1) / NB;
+                double *ps = part + (size_t)b * groups;
+                for (int g = 0; g < groups; ++g) ps[g] = 0.0;
+                for (int64_t v = v0; v < v1; ++v)
+                    for (int c = 0; c < C; ++c) {
+                        double e = gn_elem(x, x_f16, base + (size_t)v * C + c);
+                        if (pass == 0) {
+                            ps[c / cg] += e;
+                        } else {
+                            double d = e - mean[c / cg];
+                            ps[c / cg] += d * d;
+                        }
+                    }
+            }
+            for (int g = 0; g < groups; ++g) {
+                double s = 0.0;
+                for (int b = 0; b < NB; ++b) s += part[(size_t)b * groups + g];
+                if (pass == 0)
+                    mean[g] = s / cnt;
+                else
+                    var[g] = s / cnt;
+            }
+        }
+    }
+    free(part);
+    for (int64_t i = 0; i < npts; ++i) {
+        int n = (int)(vox[i] / thw), c = ch[i], g = c / cg;
+        double e = gn_elem(x, x_f16, (size_t)vox[i] * C + c);
+        double yh = (e - mean_out[(size_t)n * groups + g]) / sqrt(var_out[(size_t)n * groups + g] + eps) * gamma[c] +
+                    beta[c];
+        y[i] = apply_silu ? yh / (1.0 + exp(-yh)) : yh;
     }
     return 0;
 }

@@ -71,10 +71,19 @@ def plan_status(d):
     (dict(kh=9, pad_h=4), c3d.CONV3D_ERR_UNSUPPORTED),
     (dict(h=9000), c3d.CONV3D_ERR_UNSUPPORTED),
     (dict(n=64, t=64, h=512, w=512, c_in=8), c3d.CONV3D_ERR_UNSUPPORTED),  # 2^30 voxels
+    (dict(h=1024, w=1024), c3d.CONV3D_ERR_UNSUPPORTED),  # 3 frames x 512 ch: a 2 GiB input window
 ])
 def test_plan_rejects(bad, status):
     assert plan_status(desc(**bad)) == status
     assert c3d.conv3d_last_error() != ""
+
+
+def test_input_window_is_the_taps_reach():
+    # a causal 3x3x3 tile reads the frames its rows cover plus kt-1 = 2 more:
+    # at 512 channels and 512x512 frames that is about 0.54 GB, inside the
+    # 1 GiB one buffer resource may address
+    i = c3d.conv3d_plan(desc(t=17, h=512, w=512)).info()
+    assert i.path == c3d.CONV3D_PATH_GENERAL
 
 
 def test_plan_null_arguments():

@@ -1,4 +1,5 @@
 """Pins for the fp64 GroupNorm+SiLU oracle and the decoder-block composition (CPU only)."""
+import pytest
 import numpy as np
 import torch
 import torch.nn.functional as F
@@ -109,3 +110,31 @@ def test_decoder_block_composition():
                         padding=(0, 1, 1))
     ref = xt + conv(gn(conv(gn(xt, g1, b1), w1, c1), g2, b2), w2, c2)
     np.testing.assert_allclose(out, ref.permute(0, 2, 3, 4, 1).numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_points_variant_equals_the_full_oracle_everywhere():
+    # fp16 input read in place and fp64 input; several groups per sample, two samples
+    rng = np.random.default_rng(31)
+    for shape, groups, silu in [((2, 3, 5, 7, 64), 8, True), ((1, 130, 48), 4, False), ((3, 1, 16), 16, True)]:
+        x16 = (rng.standard_normal(shape) * 3 + 1).astype(np.float16)
+        c = shape[-1]
+        gamma, beta = rng.normal(1, 0.1, c), rng.normal(0, 0.1, c)
+        ref, mean, var = oracle.groupnorm_silu(x16.astype(np.float64), gamma, beta, groups, 1e-6, silu,
+                                               return_stats=True)
+        nvox = int(np.prod(shape[:-1]))
+        vox = np.repeat(np.arange(nvox), c)
+        ch = np.tile(np.arange(c), nvox)
+        for xin in (x16, x16.astype(np.float64)):
+            y, m, v = oracle.groupnorm_silu_points(xin, gamma, beta, groups, vox, ch, 1e-6, silu)
+            np.testing.assert_allclose(y, ref.reshape(-1), rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(m, mean, rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(v, var, rtol=1e-12)
+
+
+def test_points_variant_rejects_out_of_range_elements():
+    x = np.zeros((1, 4, 8), np.float16)
+    g, b = np.ones(8), np.zeros(8)
+    with pytest.raises(ValueError):
+        oracle.groupnorm_silu_points(x, g, b, 2, [4], [0])
+    with pytest.raises(ValueError):
+        oracle.groupnorm_silu_points(x, g, b, 2, [0], [8])

@@ -165,6 +165,14 @@ def normal_f16(ss, shape, mean=0.0, std=1.0, channel_scale=None, dtype="f16"):
     return out
 
 
+def ternary_f16(ss, shape, dtype="f16"):
+    """Values drawn uniformly from {-1, 0, 1}, in chunks (multi-GB tensors need no wide temporary)."""
+    out = np.empty(shape, _storage(dtype))
+    _fill_chunks(out.reshape(-1), ss,
+                 lambda g, s, e: _store(g.integers(-1, 2, e - s, dtype=np.int8).astype(np.float32), dtype))
+    return out
+
+
 def uniform_f16(ss, shape, bound, dtype="f16"):
     return _store(_gen(ss).uniform(-bound, bound, size=shape).astype(np.float32), dtype)
 
