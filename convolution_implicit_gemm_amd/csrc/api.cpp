@@ -268,9 +268,14 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
         return fail(CONV3D_ERR_UNSUPPORTED, "weights of 1 GiB or more");
     }
     q.w_bytes = (uint32_t)wbytes;
-    if (c3d::tile_window_voxels(q, best->bm) * q.Cin * 2 >= ((int64_t)1 << 30)) {
+    // one buffer resource addresses a tile's window: below 2 GiB for the
+    // tabulated gather (kt <= 3), below 1 GiB for the general one, whose
+    // offsets keep 30 bits
+    const int64_t window_limit = q.kt <= 3 ? ((int64_t)1 << 31) - 4096 : (int64_t)1 << 30;
+    if (c3d::tile_window_voxels(q, best->bm) * q.Cin * 2 >= window_limit) {
         delete p;
-        return fail(CONV3D_ERR_UNSUPPORTED, "one tile's input window would reach 1 GiB (frames too large)");
+        return fail(CONV3D_ERR_UNSUPPORTED, "one tile's input window would reach %s (frames too large)",
+                    q.kt <= 3 ? "2 GiB" : "1 GiB");
     }
     p->tile = best;
     p->tail = (q.Cin % best->bk) != 0;

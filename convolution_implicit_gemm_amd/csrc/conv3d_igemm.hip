@@ -125,7 +125,8 @@ __device__ __forceinline__ void dma16(buf_rsrc r, char *lds, uint32_t voff, uint
 #endif
 }
 
-// Offset that is always past a buffer's record count (records stay below 2^30).
+// Offset that is always past a buffer's record count (records stay below 2^31,
+// and the scalar offsets added to it below 2^31 too, so the sum cannot wrap).
 constexpr uint32_t kOOB = 0x80000000u;
 
 // 8-byte buffer load / store (four fp16); out-of-range loads read zeros and
@@ -372,8 +373,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
                 const bool ok = ((unsigned)ts < (unsigned)T) & ((unsigned)(a_h[j] + dr) < (unsigned)H) &
                                 ((unsigned)(a_w[j] + ds) < (unsigned)W);
                 const int rel = a_base[j] + ts * HW + rs;
-                // valid offsets are below 2^30 (the plan bounds every tile's
-                // window); invalid ones land in [2^31, 2^31 + 2^30): past the
+                // valid offsets are below 2^30 (the plan bounds the window of
+                // kernels with kt > 3 so); invalid ones land in [2^31, 2^31 + 2^30): past the
                 // records, and far enough from 2^32 that adding the scalar
                 // offset cannot wrap.  Arithmetic rather than a select, which
                 // the compiler would turn into an exec-masked block around the

@@ -118,7 +118,9 @@ typedef struct {
  * output, or an unknown t_pad_mode / flag bit; UNSUPPORTED for c_in or c_out
  * not a multiple of 8 or above 65536, kernel extents above 7, spatial extents above 8192,
  * 2^30 or more input or output voxels, weights of 1 GiB or more, or frames
- * so large that the input rows one output tile reads span 1 GiB.
+ * so large that the input rows one output tile reads span 2 GiB (1 GiB when
+ * kt > 3).  The span is about (kt - 1) frames plus a few rows: 512 channels
+ * at 512x512 or 256 channels at 1024x1024 fit with kt = 3.
  * The plan may split the K range of the tiles that do not fill a whole wave
  * of workgroups into pieces that run concurrently and leave fp32 partial
  * tiles in the workspace, summed by a second small kernel; the workspace then

@@ -84,6 +84,12 @@ def test_input_window_is_the_taps_reach():
     # 1 GiB one buffer resource may address
     i = c3d.conv3d_plan(desc(t=17, h=512, w=512)).info()
     assert i.path == c3d.CONV3D_PATH_GENERAL
+    # 256 channels at 1024x1024: a window of about 1.07 GB, inside the 2 GiB
+    # of the tabulated gather (kt <= 3) ...
+    assert c3d.conv3d_plan(desc(t=3, h=1024, w=1024, c_in=256)).info().path == c3d.CONV3D_PATH_GENERAL
+    # ... while with kt = 4 (three frames back, about 1.6 GB) it exceeds the
+    # 1 GiB of the general gather
+    assert plan_status(desc(t=4, h=1024, w=1024, c_in=256, kt=4, pad_t_front=3)) == c3d.CONV3D_ERR_UNSUPPORTED
 
 
 def test_plan_null_arguments():

@@ -4,7 +4,8 @@ Element offsets beyond 2^31 (byte offsets beyond 4 GiB): a conv whose output
 has more than 2^31 elements (8 -> 512 channels), and a 512-channel input of
 more than 2^31 elements read by the general conv (512 -> 8), by the streaming
 1x1x1 kernel (512 -> 64) and by GroupNorm+SiLU.  Channel limits: Cin = 65536
-and Cout = 65536.
+and Cout = 65536.  Input windows above 1 GiB: a 256-channel causal conv on
+1024x1024 frames.
 
 Conv data is ternary (values -1, 0, 1, small integer biases): every partial sum
 is an integer below 2^24, exact in fp32, so each fp16 output is the exact sum
@@ -127,3 +128,14 @@ def test_channel_limits_exact(cin, cout):
     ref, _ = oracle.conv3d(x.astype(np.float64), w.astype(np.float64), b.astype(np.float64), None, s.pads,
                            s.tmode, with_mag=False)
     assert np.array_equal(y.view(np.uint16), ref.astype(np.float16).view(np.uint16)), info.kernel_name
+
+
+def test_input_window_beyond_1_gib():
+    # output frame 2 reads frames 0..2: a window of 2 frames + 2 rows + 256
+    # voxels of 512 bytes, about 1.075e9 bytes, so gather offsets pass 2^30
+    s = ConvShape(1, 3, 1024, 1024, 256, 8, tmode=R)
+    x, w, b = ternary(s.x_shape, 2151), ternary(s.w_shape, 2152), small_ints(s.cout, 2153)
+    y, info = run_conv(s, x, w, b, keep_device=True)
+    assert info.path == c3d.CONV3D_PATH_GENERAL
+    m, co = sampled(s, 6000, 2154)
+    check_sampled(s, x, w, b, y, m, co, "window > 1 GiB")
