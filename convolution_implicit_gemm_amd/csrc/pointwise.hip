@@ -48,9 +48,12 @@ __device__ __forceinline__ pw_rsrc pw_make_rsrc(const void *base, uint32_t bytes
 #endif
 }
 
+// Cache policy 2 (nt): the input is streamed once.  Measured on the 256 -> 128
+// stage: 0.283 ms against 0.300 ms with the default policy; non-temporal
+// output stores, by contrast, measured 4% slower and are not used.
 __device__ __forceinline__ void pw_dma16(pw_rsrc r, char *lds, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (pw_lds_void *)lds, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (pw_lds_void *)lds, 16, voff, 0, 0, 2);
 #else
     (void)r;
     (void)lds;
