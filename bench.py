@@ -151,6 +151,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall seconds of oracle work for cpu_baseline (0 disables it)")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel extras")
+    ap.add_argument("--extras", default="all",
+                    help="comma list of per-kernel extras to run: conv256, groupnorm, bf16, t1, stage "
+                         "(the 33-frame 256x256 3x3x3 and 1x1x1 pair), or all")
     ap.add_argument("--no-calibration", action="store_true",
                     help="skip the MFMA / HBM ceiling measurements at the end")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -266,10 +269,12 @@ def main():
     result["decoder_block_config"] = ("GN(32, eps 1e-6)+SiLU -> causal conv3d 3x3x3 -> GN+SiLU -> "
                                       "causal conv3d 3x3x3 -> +x; N=1 C=256 T=17 H=W=128 fp16")
 
+    extras = {"conv256", "groupnorm", "bf16", "t1", "stage"} if args.extras == "all" else set(args.extras.split(","))
     if not args.no_kernels:
         kern = {}
         conv_flops = bp1.info().flops
 
+    if not args.no_kernels and "conv256" in extras:
         def conv_only():
             c3d.conv3d_forward(bp1, a1, bt["w1"], bt["b1"], None, c1, bws1)
         _, p = time_steps(conv_only, 10, 2, torch)
@@ -277,6 +282,7 @@ def main():
         kern["causal_conv_256_T17"] = {"ms": round(t, 4), "TFLOP/s": round(conv_flops / t / 1e9, 1),
                                        "kernel": bp1.info().kernel_name.decode()}
 
+    if not args.no_kernels and "groupnorm" in extras:
         # three input copies in rotation (428 MB > the 256 MB MALL), so no call
         # finds its input already cached by the previous one
         gx = [bx, bx.clone(), bx.clone()]
@@ -297,6 +303,7 @@ def main():
                                           "inputs": "3 copies in rotation"}
         del gx
 
+    if not args.no_kernels and "bf16" in extras:
         # the headline conv with bf16 operands (CONV3D_F_BF16)
         d1b = workloads.conv_inputs(s1, 1001, dtype="bf16")
         pb = c3d.conv3d_plan(desc_of(c3d, s1, c3d.CONV3D_F_BIAS | c3d.CONV3D_F_BF16))
@@ -315,6 +322,7 @@ def main():
                                            "kernel": pb.info().kernel_name.decode()}
         del xb, wb, bb, yb, wsb, d1b
 
+    if not args.no_kernels and "t1" in extras:
         s1f = workloads.CAUSAL_256_T1
         pt1 = c3d.conv3d_plan(desc_of(c3d, s1f, c3d.CONV3D_F_BIAS))
         ws1 = ws_for(pt1, torch, dev)
@@ -328,8 +336,10 @@ def main():
         kern["first_frame_fold_256"] = {"us": round(t * 1e3, 2),
                                         "TFLOP/s_folded": round(pt1.info().flops / t / 1e9, 1),
                                         "path": int(pt1.info().path)}
-        del x1, y1, ws1, a1, c1, a2, out, bx
+        del x1, y1, ws1
+    del a1, c1, a2, out, bx
 
+    if not args.no_kernels and "stage" in extras:
         log("channel-changing stage (2.2 GB input)")
         d3 = workloads.workload_inputs(3)
         s3, s3b = d3["shape"], d3["shape2"]
@@ -360,6 +370,7 @@ def main():
                                                   "frac_of_hbm": round(pw_bytes / t / 1e6 / PEAK_HBM_GBS, 3),
                                                   "kernel": p3b.info().kernel_name.decode()}
         del x3, y3, y3b
+    if not args.no_kernels:
         result["kernels"] = kern
 
     if args.cpu_seconds > 0:
