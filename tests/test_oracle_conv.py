@@ -24,6 +24,10 @@ GEOMS = [
     (1, 3, 3, (0, 0, 1, 1), Z),   # spatial-only
     (3, 1, 1, (2, 0, 0, 0), R),   # temporal-only causal
     (3, 3, 3, (1, 1, 1, 1), R),   # symmetric replicate in time
+    (5, 3, 3, (4, 0, 1, 1), R),   # causal kt = 5
+    (4, 5, 7, (1, 2, 2, 3), Z),   # mixed extents, asymmetric temporal padding
+    (1, 7, 7, (0, 0, 3, 3), Z),   # 7x7 spatial
+    (2, 2, 2, (1, 0, 1, 0), Z),   # even extents: one more output row than input rows
 ]
 
 
