@@ -385,18 +385,21 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
         }
     };
     // weights of the stage at the cursor into weight buffer wbuf
-    auto fire_w = [&](int wbuf) {
+    // (s_w, ci: the scalar offset and channel slice of the stage, taken from
+    // the cursor, possibly before the cursor moved on)
+    auto fire_w_at = [&](int wbuf, uint32_t s_w, int ci) {
         char *sb = smem + wbuf * W_BYTES;
-        const uint32_t s_w = (uint32_t)(ld_tap * Cin + ld_ci) * 2u;
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
             const int q = j * NW + wv;
             if (QB % NW == 0 || q < QB) {
-                const uint32_t v = (!TAIL || ld_ci + b_c8[j] < Cin) ? b_voff[j] : kOOB;
+                const uint32_t v = (!TAIL || ci + b_c8[j] < Cin) ? b_voff[j] : kOOB;
                 dma16(wr, sb + q * 1024, v, s_w);
             }
         }
     };
+    auto w_soff = [&] { return (uint32_t)(ld_tap * Cin + ld_ci) * 2u; };
+    auto fire_w = [&](int wbuf) { fire_w_at(wbuf, w_soff(), ld_ci); };
     // activations of the stage at the cursor (offsets from set_offsets) into
     // activation buffer abuf; PART < 0: every load, else only the loads that
     // belong to k-step PART when the fetch is spread over KS - 1 k-steps
@@ -509,6 +512,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
 
     int wbuf = 0, abuf = 0;  // buffers of stage it
     int afill = STAGES % ASTAGES;  // D = 1: buffer of stage it+STAGES
+    uint32_t pend_sw = 0;  // D = 1: the weight stage fetched at the coming barrier
+    int pend_ci = 0;
     for (int it = it0; it < it1; ++it) {
         // region A: k-steps 1..KS-1 of this stage are read, 0..KS-2 multiplied
         static_for<KS - 1>([&](auto kk) {
@@ -517,6 +522,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
                 raise_prio();
                 fire_a(afill, kk);
                 lower_prio();
+                // With the spread fetch the cursor is free once the stage's
+                // last activation load is issued: move it on here, among the
+                // MFMAs, rather than after the barrier, where every wave of a
+                // SIMD would run the ~40 scalar instructions at once while the
+                // matrix unit waits (measured: +1% on every shape).
+                if constexpr (decltype(kk)::value == KS - 2) {
+                    pend_sw = w_soff();
+                    pend_ci = ld_ci;
+                    advance();
+                    set_offsets();
+                }
             }
             mfmas(kk & 1);
         });
@@ -525,11 +541,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void conv3d_igemm_kerne
         // region B: refill this stage's buffers, read k-step 0 of the next
         // stage, and run the last k-step of this one meanwhile
         raise_prio();
-        if constexpr (D == 0) fire_a(abuf, all_loads{});
-        fire_w(wbuf);
-        lower_prio();
-        advance();
-        set_offsets();
+        if constexpr (D == 1) {
+            fire_w_at(wbuf, pend_sw, pend_ci);
+            lower_prio();
+        } else {
+            fire_a(abuf, all_loads{});
+            fire_w(wbuf);
+            lower_prio();
+            advance();
+            set_offsets();
+        }
         if constexpr (D == 1) afill = abuf;
         wbuf = wbuf + 1 == STAGES ? 0 : wbuf + 1;
         abuf = abuf + 1 == ASTAGES ? 0 : abuf + 1;
