@@ -40,7 +40,7 @@ EXPORTED = ("conv3d_plan", "conv3d_plan_query", "conv3d_plan_destroy", "conv3d_f
             "groupnorm_silu_workspace", "groupnorm_silu", "groupnorm_silu_bf16",
             "conv3d_calibrate_scratch_bytes",
             "conv3d_calibrate_mfma", "conv3d_calibrate_hbm", "conv3d_status_str",
-            "conv3d_last_error", "conv3d_version")
+            "conv3d_last_error", "conv3d_version", "conv3d_selftest")
 
 
 class conv3d_desc(ctypes.Structure):
@@ -106,6 +106,8 @@ def load_library(path: str = LIB_PATH):
     lib.conv3d_last_error.restype = ctypes.c_char_p
     lib.conv3d_version.argtypes = []
     lib.conv3d_version.restype = i32
+    lib.conv3d_selftest.argtypes = []
+    lib.conv3d_selftest.restype = i32
     dp = ctypes.POINTER(ctypes.c_double)
     lib.conv3d_calibrate_scratch_bytes.argtypes = []
     lib.conv3d_calibrate_scratch_bytes.restype = sz
@@ -261,3 +263,21 @@ def conv3d_last_error() -> str:
 
 def conv3d_version() -> int:
     return load_library().conv3d_version()
+
+
+def conv3d_selftest() -> int:
+    """Run the library's start-up self-test on the current device (0 = pass)."""
+    return load_library().conv3d_selftest()
+
+
+def selftest_in_subprocess(timeout: float = 300.0) -> int:
+    """conv3d_selftest() in a child process, so that a broken driver or device
+    cannot take this process down.  Returns the child's exit status: 0 = pass,
+    a conv3d_status or 16 + case number as conv3d_selftest documents,
+    negative for a child killed by a signal."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import convolution_implicit_gemm_amd as c; "
+            "rc = c.conv3d_selftest(); sys.stderr.write(c.conv3d_last_error() + '\\n'); sys.exit(rc)"
+            % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    return subprocess.run([sys.executable, "-c", code], timeout=timeout).returncode

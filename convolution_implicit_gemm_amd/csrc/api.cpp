@@ -31,6 +31,17 @@ conv3d_status ok() {
     return CONV3D_OK;
 }
 
+}  // namespace
+
+void c3d::set_last_error(const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+}
+
+namespace {
+
 constexpr int64_t kMaxVoxels = (int64_t)1 << 30;
 constexpr int kMaxSpatial = 8192;
 constexpr int kMaxKernel = 7;

@@ -99,4 +99,7 @@ hipError_t calibrate_mfma(void *scratch, hipStream_t s, double *tflops, double *
 hipError_t calibrate_hbm(const void *src, void *dst, size_t bytes, hipStream_t s, double *read_gbs,
                          double *copy_gbs);
 
+// Set the calling thread's conv3d_last_error() message (printf format).
+void set_last_error(const char *fmt, ...);
+
 }  // namespace c3d

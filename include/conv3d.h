@@ -227,6 +227,24 @@ conv3d_status conv3d_calibrate_hbm(const void *src, void *dst, size_t bytes, dou
                                    void *stream);
 
 /* Static text for a status code. */
+/*
+ * Start-up self-test of this library on the current device: tiny
+ * integer-valued cases (causal conv with bias and residual, zero-padded conv,
+ * the streaming 1x1x1 kernel, the T=1 fold, a plan that splits K, and
+ * GroupNorm+SiLU) run through the entry points above and are compared with
+ * scalar loops inside this call: convs bit for bit, GroupNorm within 1e-3
+ * relative + 2^-14 absolute.  The boundary's own behaviour, specified by the
+ * "fall back, self-test in a subprocess" convention of the pages' native
+ * fork: a process that must survive a broken driver or device calls this in
+ * a child process before relying on the library.
+ * Returns 0 if every case passes; a conv3d_status (1..5) if a call failed,
+ * e.g. CONV3D_ERR_NO_DEVICE without a gfx950 device; 16 + k if case k
+ * produced wrong values (k = 5: GroupNorm; 6: no case split K).
+ * conv3d_last_error() names the case.  Unlike every other entry point except
+ * the calibration calls, it allocates device memory and synchronises.
+ */
+int32_t conv3d_selftest(void);
+
 const char *conv3d_status_str(conv3d_status s);
 
 /* Message of the last failure on the calling thread ("" if none). */

@@ -275,3 +275,9 @@ def test_chunk_without_a_device_reports_no_device():
     p = c3d.conv3d_plan(desc(flags=c3d.CONV3D_F_CHUNK | c3d.CONV3D_F_BIAS))
     assert lib.conv3d_forward_chunk(p.handle, A + 768 * MB, A, A + 128 * MB, A + 192 * MB, None, A + 256 * MB,
                                     A + 512 * MB, p.workspace_bytes, None) == c3d.CONV3D_ERR_NO_DEVICE
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="host without a GPU only")
+def test_selftest_without_a_device_reports_no_device():
+    assert c3d.conv3d_selftest() == c3d.CONV3D_ERR_NO_DEVICE
+    assert "device" in c3d.conv3d_last_error()
