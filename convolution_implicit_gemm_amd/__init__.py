@@ -158,6 +158,13 @@ class Plan:
             self.handle = None
 
 
+def weight_from_ncdhw(weight):
+    """A torch Conv3d weight [Cout][Cin][kt][kh][kw] in this library's layout
+    [Cout][kt][kh][kw][Cin] (a contiguous copy).  A load-time conversion, done
+    once per weight, off the forward path."""
+    return weight.permute(0, 2, 3, 4, 1).contiguous()
+
+
 def make_desc(n, t, h, w, c_in, c_out, kt=3, kh=3, kw=3, pad_t_front=1, pad_t_back=1, pad_h=1,
               pad_w=1, t_pad_mode=CONV3D_TPAD_ZERO, flags=0) -> conv3d_desc:
     return conv3d_desc(n, t, h, w, c_in, c_out, kt, kh, kw, pad_t_front, pad_t_back, pad_h, pad_w,

@@ -281,3 +281,22 @@ def test_chunk_without_a_device_reports_no_device():
 def test_selftest_without_a_device_reports_no_device():
     assert c3d.conv3d_selftest() == c3d.CONV3D_ERR_NO_DEVICE
     assert "device" in c3d.conv3d_last_error()
+
+
+def test_weight_from_ncdhw_matches_torch_conv3d_layout():
+    # torch's Conv3d keeps [Cout][Cin][kt][kh][kw] and NCDHW activations; the
+    # helper's [Cout][kt][kh][kw][Cin] with NDHWC activations must give the
+    # same correlation (checked through the fp64 oracle, zero padding 1)
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+    import oracle
+    g = torch.Generator().manual_seed(7)
+    w = torch.randn(6, 5, 3, 2, 3, generator=g, dtype=torch.float64)
+    x = torch.randn(2, 5, 4, 6, 7, generator=g, dtype=torch.float64)
+    ref = F.conv3d(x, w, padding=(1, 1, 1)).permute(0, 2, 3, 4, 1).numpy()
+    w_ours = c3d.weight_from_ncdhw(w)
+    assert tuple(w_ours.shape) == (6, 3, 2, 3, 5) and w_ours.is_contiguous()
+    got, _ = oracle.conv3d(x.permute(0, 2, 3, 4, 1).numpy(), w_ours.numpy(), pads=(1, 1, 1, 1),
+                           tmode=oracle.TPAD_ZERO)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
