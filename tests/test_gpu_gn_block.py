@@ -47,6 +47,10 @@ GN_CASES = [  # (n, thw_shape, c, groups, mean, std)
     (1, (1, 1, 3), 512, 32, 0.0, 1.0),
     (3, (5, 4, 4), 128, 1, 0.0, 1.0),
     (1, (2, 64, 64), 512, 32, 100.0, 1.0),  # large mean: the statistics must not cancel
+    (2, (1, 1, 1), 64, 8, 0.0, 1.0),          # one voxel per sample: 8 values per group
+    (1, (3, 3, 3), 8, 1, 0.0, 1.0),           # the fewest channels: 8 in one group
+    (1, (1, 13, 17), 96, 12, -2.0, 0.5),      # odd voxel count, 8-channel groups
+    (1, (1, 2, 3), 8192, 32, 0.0, 1.0),       # the most channels
 ]
 
 
@@ -74,7 +78,7 @@ def test_in_place_and_workspace_reuse():
     d = workloads.gn_inputs(1, (3, 16, 16), 256, 902)
     need = c3d.groupnorm_silu_workspace(1, 3 * 256, 256, 32)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
-    for rep in range(3):  # the counter in the workspace must come back to zero each call
+    for rep in range(3):  # nothing of an earlier call's workspace may leak into the next
         x = d["x"] * np.float16(1 + rep)
         y = gn_gpu(x, d["gamma"], d["beta"], 32, ws=ws, in_place=(rep == 2)).cpu().numpy()
         ref = oracle.groupnorm_silu(x, d["gamma"], d["beta"], 32, 1e-6, True)
