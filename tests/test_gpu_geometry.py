@@ -89,3 +89,24 @@ def test_k_split_on_the_general_gather():
     assert i1.split_tiles > 0 and i1.split_pieces >= 2
     ref, _ = oracle_of(s, x, w, b)
     assert np.array_equal(y1.astype(np.float64), ref)
+
+
+DEGENERATE = [
+    ConvShape(1, 1, 1, 1, 8, 8),                                   # one voxel (T=1: folded)
+    ConvShape(2, 1, 1, 1, 16, 24, tmode=Z),                        # one voxel per sample, zero-causal fold
+    ConvShape(1, 5, 1, 37, 16, 8),                                 # one-row frames: only r = 1 reads
+    ConvShape(1, 4, 29, 1, 8, 16),                                 # one-column frames
+    ConvShape(1, 5, 6, 7, 8, 8),                                   # the fewest channels
+    ConvShape(1, 3, 3, 3, 16, 8, pad_t_front=0, pad_t_back=0, pad_h=0, pad_w=0, tmode=Z),  # one output voxel
+]
+
+
+@pytest.mark.parametrize("case", range(len(DEGENERATE)))
+def test_degenerate_shapes_bit_exact(case):
+    s = DEGENERATE[case]
+    x, w, b = ternary(s.x_shape, 3600 + case), ternary(s.w_shape, 3610 + case), small_ints(s.cout, 3620 + case)
+    ref, _ = oracle_of(s, x, w, b)
+    y, info = run_conv(s, x, w, b)
+    assert np.array_equal(y.astype(np.float64), ref), info.kernel_name
+    yg, ig = run_conv(s, x, w, b, flags=c3d.CONV3D_F_NO_T1_FASTPATH)
+    assert ig.path == c3d.CONV3D_PATH_GENERAL and np.array_equal(yg, y)
