@@ -282,11 +282,12 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
     // one buffer resource addresses a tile's window: below 2 GiB for the
     // tabulated gather (kt <= 3), below 1 GiB for the general one, whose
     // offsets keep 30 bits
-    const int64_t window_limit = q.kt <= 3 ? ((int64_t)1 << 31) - 4096 : (int64_t)1 << 30;
+    const bool tabulated = q.kt <= 3;
+    const int64_t window_limit = tabulated ? ((int64_t)1 << 31) - 4096 : (int64_t)1 << 30;
     if (c3d::tile_window_voxels(q, best->bm) * q.Cin * 2 >= window_limit) {
-        delete p;
+        delete p;  // q refers into *p: nothing below may read it
         return fail(CONV3D_ERR_UNSUPPORTED, "one tile's input window would reach %s (frames too large)",
-                    q.kt <= 3 ? "2 GiB" : "1 GiB");
+                    tabulated ? "2 GiB" : "1 GiB");
     }
     p->tile = best;
     p->tail = (q.Cin % best->bk) != 0;
