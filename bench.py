@@ -153,7 +153,8 @@ def main():
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel extras")
     ap.add_argument("--extras", default="all",
                     help="comma list of per-kernel extras to run: conv256, groupnorm, bf16, t1, stage "
-                         "(the 33-frame 256x256 3x3x3 and 1x1x1 pair), or all")
+                         "(the 33-frame 256x256 3x3x3 and 1x1x1 pair), gemm (the vendor GEMM on the "
+                         "headline's M x N x K, for context), or all")
     ap.add_argument("--no-calibration", action="store_true",
                     help="skip the MFMA / HBM ceiling measurements at the end")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -269,7 +270,8 @@ def main():
     result["decoder_block_config"] = ("GN(32, eps 1e-6)+SiLU -> causal conv3d 3x3x3 -> GN+SiLU -> "
                                       "causal conv3d 3x3x3 -> +x; N=1 C=256 T=17 H=W=128 fp16")
 
-    extras = {"conv256", "groupnorm", "bf16", "t1", "stage"} if args.extras == "all" else set(args.extras.split(","))
+    extras = ({"conv256", "groupnorm", "bf16", "t1", "stage", "gemm"} if args.extras == "all"
+              else set(args.extras.split(",")))
     if not args.no_kernels:
         kern = {}
         conv_flops = bp1.info().flops
@@ -338,6 +340,23 @@ def main():
                                         "path": int(pt1.info().path)}
         del x1, y1, ws1
     del a1, c1, a2, out, bx
+
+    if not args.no_kernels and "gemm" in extras:
+        # context only ("FLOPs parity"): the vendor GEMM (torch.matmul on
+        # hipBLASLt) on a dense fp16 matrix of the headline's im2col shape,
+        # M x K times K x N.  The conv never builds such a matrix.
+        gm, gk, gn = info.gemm_m, info.gemm_k, info.gemm_n
+        ga = torch.randn(gm, gk, device=dev, dtype=torch.float16)
+        gb = torch.randn(gk, gn, device=dev, dtype=torch.float16)
+        gc = torch.empty(gm, gn, device=dev, dtype=torch.float16)
+
+        def gemm():
+            torch.matmul(ga, gb, out=gc)
+        _, p = time_steps(gemm, 30, 10, torch)
+        t = sum(p) / len(p)
+        kern["vendor_gemm_same_mnk"] = {"ms": round(t, 4), "TFLOP/s": round(2.0 * gm * gn * gk / t / 1e9, 1),
+                                        "shape_m_k_n": [gm, gk, gn], "gemm_ms_over_conv_ms": round(t / kernel_ms, 3)}
+        del ga, gb, gc
 
     if not args.no_kernels and "stage" in extras:
         log("channel-changing stage (2.2 GB input)")
