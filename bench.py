@@ -113,8 +113,9 @@ def cpu_baseline_leg(d, y_dev, info, target_s, np):
         ref, mag = oracle.conv3d_points(x64, w64, b64, None, s.pads, s.tmode, m, co)
         return time.perf_counter() - t0, m, co, ref, mag
 
-    dt, *_ = run(8)
-    per_vox = max(dt / 8, 1e-6)
+    # size the sample from a probe large enough that thread start-up does not dominate it
+    dt, *_ = run(64)
+    per_vox = max(dt / 64, 1e-6)
     nvox = int(min(m_total, max(16, target_s / per_vox)))
     dt, m, co, ref, mag = run(nvox)
     flops = 2.0 * k * m.size
@@ -148,7 +149,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first; the clocks need ~50 ms of load to settle")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall seconds of oracle work for cpu_baseline (0 disables it)")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel extras")
     ap.add_argument("--extras", default="all",
