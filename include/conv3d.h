@@ -15,13 +15,14 @@
  * item 4286, paragraph on MPS tweaks and the fused kernel).
  *
  * Conventions shared by every entry point:
- *  - No entry point aborts or throws, and none but the two measurement aids
- *    at the end synchronises the device.  Work is enqueued on the caller's
+ *  - No entry point aborts or throws, and none but the measurement aids and
+ *    the self-test at the end synchronises the device.  Work is enqueued on the caller's
  *    stream (a hipStream_t passed as void*; NULL is the default stream), after
  *    the A1111 Metal fork's lesson that a native op must go into the
  *    framework's current stream without its own commit.
- *  - The caller owns every device buffer.  The library never allocates
- *    device memory.  Device pointers must be 16-byte aligned.
+ *  - The caller owns every device buffer.  Apart from the self-test, the
+ *    library never allocates device memory.  Device pointers must be 16-byte
+ *    aligned.
  *  - All tensors are fp16 (IEEE binary16), or bf16 (the upper half of an IEEE
  *    binary32) where stated; accumulation is fp32 and each output is
  *    rounded once, to nearest even.
@@ -226,17 +227,17 @@ conv3d_status conv3d_calibrate_mfma(void *scratch, size_t scratch_bytes, double 
 conv3d_status conv3d_calibrate_hbm(const void *src, void *dst, size_t bytes, double *read_gbs, double *copy_gbs,
                                    void *stream);
 
-/* Static text for a status code. */
 /*
  * Start-up self-test of this library on the current device: tiny
  * integer-valued cases (causal conv with bias and residual, zero-padded conv,
  * the streaming 1x1x1 kernel, the T=1 fold, a plan that splits K, and
  * GroupNorm+SiLU) run through the entry points above and are compared with
  * scalar loops inside this call: convs bit for bit, GroupNorm within 1e-3
- * relative + 2^-14 absolute.  The boundary's own behaviour, specified by the
- * "fall back, self-test in a subprocess" convention of the pages' native
- * fork: a process that must survive a broken driver or device calls this in
- * a child process before relying on the library.
+ * relative + 2^-14 absolute.  The A1111 Metal fork write-up (news.bugfactory.tech
+ * item 4286) runs its native code's self-test in a subprocess at start-up, and
+ * falls back to the framework when it fails; in the same way, a process that
+ * must survive a broken driver or device calls this in a child process before
+ * relying on the library.
  * Returns 0 if every case passes; a conv3d_status (1..5) if a call failed,
  * e.g. CONV3D_ERR_NO_DEVICE without a gfx950 device; 16 + k if case k
  * produced wrong values (k = 5: GroupNorm; 6: no case split K).
@@ -245,6 +246,7 @@ conv3d_status conv3d_calibrate_hbm(const void *src, void *dst, size_t bytes, dou
  */
 int32_t conv3d_selftest(void);
 
+/* Static text for a status code. */
 const char *conv3d_status_str(conv3d_status s);
 
 /* Message of the last failure on the calling thread ("" if none). */
