@@ -339,10 +339,10 @@ conv3d_status conv3d_plan_query(conv3d_plan_t p, conv3d_plan_info *info) {
     if (p->streaming) {
         const c3d::PwGeom g = c3d::pointwise_geometry(p->prm.Cin, p->prm.Cout, p->prm.M);
         info->tile_m = g.rows;
-        info->tile_n = 128;
+        info->tile_n = 32 * g.waves;
         info->tile_k = p->prm.Cin;
         info->stages = g.ring;
-        info->threads = 256;
+        info->threads = 64 * g.waves;
         info->grid = g.grid_x * g.grid_y;
         snprintf(info->kernel_name, sizeof(info->kernel_name), "conv1x1_stream_cin%d", p->prm.Cin);
         return ok();

@@ -77,8 +77,9 @@ hipError_t launch_pointwise(const PwParams &p, hipStream_t s);
 struct PwGeom {
     int rows;        // voxels per tile
     int ring;        // LDS ring depth, in tiles
+    int waves;       // waves per block, 32 output channels each
     int64_t grid_x;  // persistent blocks along the voxels
-    int64_t grid_y;  // blocks of 128 output channels
+    int64_t grid_y;  // blocks of 32 * waves output channels
 };
 PwGeom pointwise_geometry(int32_t cin, int32_t cout, int64_t m);
 

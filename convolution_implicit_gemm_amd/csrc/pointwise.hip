@@ -83,7 +83,11 @@ __device__ __forceinline__ int pw_swz(int row) {
 }
 
 constexpr int kPwRows = 64;   // voxels per tile
-constexpr int kPwWaves = 4;   // 4 x 32 output channels per block
+// Waves per block, each owning 32 output channels: 4 up to 128 output
+// channels, 8 above, so that one block row covers up to 256 channels and the
+// input is streamed once (with 4 waves a 512 -> 256 conv streamed it twice and
+// ran at a third of the HBM rate).
+constexpr int pw_waves(int32_t cout) { return cout > 128 ? 8 : 4; }
 
 // Input ring depth: about 64 KB of tiles per block, at most 8.
 template <int CIN>
@@ -93,26 +97,27 @@ constexpr int pw_ring() {
     return nb > 8 ? 8 : (nb < 2 ? 2 : nb);
 }
 
-template <int CIN, typename E>
-__global__ __launch_bounds__(256, 2) void pointwise_kernel(PwParams p) {
+template <int CIN, int NWV, typename E>
+__global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void pointwise_kernel(PwParams p) {
     constexpr int RB = CIN * 2;                 // bytes per input row
     constexpr int CPR = CIN / 8;                // 16-byte chunks per row
     constexpr int BM = kPwRows;                 // rows per tile
     constexpr int NB = pw_ring<CIN>();          // ring depth
     constexpr int TILE_BYTES = BM * RB;
     constexpr int RPI = 1024 / RB;              // rows per 1 KiB load instruction
-    constexpr int NI = TILE_BYTES / 1024 / kPwWaves;  // load instructions per wave per tile
+    constexpr int NI = TILE_BYTES / 1024 / NWV;  // load instructions per wave per tile
     constexpr int KF = CIN / 16;                // MFMA k-steps
     constexpr int SUB = BM / 32;                // 32-voxel sub-tiles per tile
     static_assert(BM % 32 == 0, "tiles of whole 32-voxel sub-tiles");
-    static_assert(RB <= 1024 && 1024 % RB == 0 && NI >= 1, "CIN in {64, 128, 256, 512}");
+    static_assert(RB <= 1024 && 1024 % RB == 0 && NI >= 1 && (TILE_BYTES / 1024) % NWV == 0,
+                  "CIN in {64, 128, 256, 512}, whole load instructions per wave");
 
     __shared__ __attribute__((aligned(1024))) char smem[NB * TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char obuf[kPwWaves * BM * 64];  // output staging
+    __shared__ __attribute__((aligned(1024))) char obuf[NWV * BM * 64];  // output staging
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int co0 = blockIdx.y * (32 * kPwWaves) + wv * 32;
+    const int co0 = blockIdx.y * (32 * NWV) + wv * 32;
     const bool live = co0 < p.Cout;  // wave-uniform
     const int rrow = lane & 31, rhi = lane >> 5;
 
@@ -130,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void pointwise_kernel(PwParams p) {
     uint32_t voff[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-        const int q = j * kPwWaves + wv;
+        const int q = j * NWV + wv;
         const int row = q * RPI + lane / CPR;
         const int c = (lane % CPR) ^ pw_swz<CPR>(row);
         voff[j] = (uint32_t)(row * RB + c * 16);
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void pointwise_kernel(PwParams p) {
         const pw_rsrc r = pw_make_rsrc(p.x + (int64_t)(tile < ntiles ? m0 : 0) * CIN, (uint32_t)(rows * RB));
         char *sb = smem + buf * TILE_BYTES;
 #pragma unroll
-        for (int j = 0; j < NI; ++j) pw_dma16(r, sb + (j * kPwWaves + wv) * 1024, voff[j]);
+        for (int j = 0; j < NI; ++j) pw_dma16(r, sb + (j * NWV + wv) * 1024, voff[j]);
     };
 
     const int step = (int)gridDim.x;
@@ -241,27 +246,40 @@ __global__ __launch_bounds__(256, 2) void pointwise_kernel(PwParams p) {
 
 template <int CIN>
 PwGeom pw_geom(int32_t cout, int64_t m) {
-    // as many resident blocks as LDS allows, up to four per CU
-    constexpr int lds = pw_ring<CIN>() * kPwRows * CIN * 2 + kPwWaves * kPwRows * 64;
-    constexpr int per_cu = (160 * 1024 / lds) < 4 ? (160 * 1024 / lds) : 4;
+    // persistent blocks, all resident: as many as LDS allows up to four per CU
+    // with 4 waves; one per CU with 8 waves (its launch bounds, which keep the
+    // 512-channel weights in registers)
+    const int nwv = pw_waves(cout);
+    const int lds = pw_ring<CIN>() * kPwRows * CIN * 2 + nwv * kPwRows * 64;
+    const int by_lds = 160 * 1024 / lds;
+    const int per_cu = nwv == 8 ? 1 : (by_lds < 4 ? by_lds : 4);
     const int64_t ntiles = (m + kPwRows - 1) / kPwRows;
-    const int64_t cap = 256 * per_cu;
+    const int64_t cap = 256 * (int64_t)per_cu;
     PwGeom g;
     g.rows = kPwRows;
     g.ring = pw_ring<CIN>();
+    g.waves = nwv;
     g.grid_x = ntiles < cap ? ntiles : cap;
-    g.grid_y = (cout + 32 * kPwWaves - 1) / (32 * kPwWaves);
+    g.grid_y = (cout + 32 * nwv - 1) / (32 * nwv);
     return g;
+}
+
+template <int CIN, int NWV>
+void launch_pw_w(const PwParams &p, dim3 grid, hipStream_t s) {
+    if (p.bf16)
+        hipLaunchKernelGGL((pointwise_kernel<CIN, NWV, __bf16>), grid, dim3(64 * NWV), 0, s, p);
+    else
+        hipLaunchKernelGGL((pointwise_kernel<CIN, NWV, _Float16>), grid, dim3(64 * NWV), 0, s, p);
 }
 
 template <int CIN>
 hipError_t launch_pw(const PwParams &p, hipStream_t s) {
     const PwGeom g = pw_geom<CIN>(p.Cout, p.M);
     const dim3 grid((unsigned)g.grid_x, (unsigned)g.grid_y);
-    if (p.bf16)
-        hipLaunchKernelGGL((pointwise_kernel<CIN, __bf16>), grid, dim3(64 * kPwWaves), 0, s, p);
+    if (g.waves == 8)
+        launch_pw_w<CIN, 8>(p, grid, s);
     else
-        hipLaunchKernelGGL((pointwise_kernel<CIN, _Float16>), grid, dim3(64 * kPwWaves), 0, s, p);
+        launch_pw_w<CIN, 4>(p, grid, s);
     return hipGetLastError();
 }
 

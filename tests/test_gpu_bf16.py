@@ -93,17 +93,17 @@ def test_bf16_first_frame_fold(tmode):
     assert np.array_equal(yf, yg)
 
 
-@pytest.mark.parametrize("cin", [64, 128, 256, 512])
-def test_bf16_pointwise(cin):
-    s = ConvShape(2, 3, 9, 10, cin, 128, kt=1, kh=1, kw=1, pad_t_front=0, pad_t_back=0, pad_h=0, pad_w=0,
+@pytest.mark.parametrize("cin,cout", [(64, 128), (128, 128), (256, 128), (512, 128), (256, 384)])
+def test_bf16_pointwise(cin, cout):
+    s = ConvShape(2, 3, 9, 10, cin, cout, kt=1, kh=1, kw=1, pad_t_front=0, pad_t_back=0, pad_h=0, pad_w=0,
                   tmode=Z)
-    x, w = ternary_bf16(s.x_shape, 740 + cin), ternary_bf16(s.w_shape, 741 + cin)
+    x, w = ternary_bf16(s.x_shape, 740 + cin + cout), ternary_bf16(s.w_shape, 741 + cin + cout)
     y, info = run_conv(s, x, w)
     assert info.kernel_name.decode().startswith("conv1x1_stream")
     ref, _ = oracle_full(s, x, w)
     assert np.array_equal(y, rounded(ref))
-    d = workloads.conv_inputs(s, 750 + cin, dtype="bf16")
-    res = workloads.normal_f16(np.random.SeedSequence(751 + cin), out_dims(s), dtype="bf16")
+    d = workloads.conv_inputs(s, 750 + cin + cout, dtype="bf16")
+    res = workloads.normal_f16(np.random.SeedSequence(751 + cin + cout), out_dims(s), dtype="bf16")
     y, _ = run_conv(s, d["x"], d["w"], d["b"], res=res)
     ref, mag = oracle_full(s, d["x"], d["w"], d["b"], res)
     assert_conv_close(f64(y), ref, mag, "bf16 pointwise + residual", ulp=ulp_bf16)

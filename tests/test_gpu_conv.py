@@ -229,7 +229,7 @@ def test_channel_changing_stage_full_size_sampled():
     check_sampled(s2, d2, y2, count=20000, seed=15)
 
 
-PW_CASES = [(64, 32), (128, 160), (256, 128), (512, 96), (256, 256)]
+PW_CASES = [(64, 32), (128, 160), (256, 128), (512, 96), (256, 256), (512, 512), (64, 288)]
 
 
 @pytest.mark.parametrize("cin,cout", PW_CASES)
