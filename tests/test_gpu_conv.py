@@ -249,6 +249,36 @@ def test_streaming_pointwise_exact(cin, cout):
     assert np.array_equal(yg, y)
 
 
+# Several tiles per persistent block (the input ring wraps) and a ragged last
+# tile: M = 3*181*191 = 103713 voxels, above 3 tiles per block for every
+# configuration.  (cin, cout, residual): 4- and 8-wave blocks, the 32-row
+# tiles at 512 input channels, and the residual epilogue.
+PW_RING_CASES = [(64, 64, False), (128, 64, False), (256, 128, False), (256, 128, True), (256, 256, False),
+                 (512, 128, True), (512, 256, False)]
+
+
+@pytest.mark.parametrize("cin,cout,with_res", PW_RING_CASES)
+def test_streaming_pointwise_ring_wraps_exact(cin, cout, with_res):
+    s = ConvShape(1, 3, 181, 191, cin, cout, kt=1, kh=1, kw=1, pad_t_front=0, pad_t_back=0, pad_h=0,
+                  pad_w=0, tmode=Z)
+    x = ternary(s.x_shape, 70 + cin)
+    w = ternary(s.w_shape, 71 + cout)
+    b = np.random.default_rng(72).integers(-2, 3, s.cout).astype(np.float16)
+    res = np.random.default_rng(73).integers(-3, 4, out_dims(s)).astype(np.float16) if with_res else None
+    y, info = run_conv(s, x, w, b, res=res)
+    assert info.kernel_name.decode() == "conv1x1_stream_cin%d" % cin
+    m_total = s.n * s.t * s.h * s.w
+    assert m_total // info.tile_m > 3 * info.grid
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(m_total - 40, m_total),
+                                     np.random.default_rng(74).integers(0, m_total, 192)]))
+    m = np.repeat(rows, cout)
+    co = np.tile(np.arange(cout), rows.size)
+    ref, _ = oracle.conv3d_points(x, w, b, res, s.pads, s.tmode, m, co)
+    got = y.reshape(-1, cout)[m, co]
+    assert np.array_equal(got.astype(np.float64), ref), "%d of %d sampled outputs differ" % (
+        int((got.astype(np.float64) != ref).sum()), m.size)
+
+
 def test_streaming_pointwise_bias_residual_bound():
     s = ConvShape(1, 4, 9, 11, 256, 128, kt=1, kh=1, kw=1, pad_t_front=0, pad_t_back=0, pad_h=0,
                   pad_w=0, tmode=Z)
