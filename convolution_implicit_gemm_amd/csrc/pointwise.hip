@@ -199,6 +199,22 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void pointwise_kernel(P
     for (; tile < ntiles; tile += step) {
         // this tile landed; everyone is done with the buffer refilled next
         pw_wait_and_barrier<(NB - 2) * NI>();
+        // this tile's residual, fetched before the next tile's loads: loads
+        // retire in order, so waiting for it in the epilogue leaves those in
+        // flight (fetched after them, it would drain the ring)
+        const int m0 = tile * BM;
+        pw_half4 rv[SUB][4];
+        if (p.res && live) {
+#pragma unroll
+            for (int u = 0; u < SUB; ++u)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int vrow = u * 32 + rrow;
+                    rv[u][g] = m0 + vrow < M ? *reinterpret_cast<const pw_half4 *>(
+                                                   p.res + (int64_t)(m0 + vrow) * p.Cout + co0 + 8 * g + 4 * rhi)
+                                             : pw_half4{};
+                }
+        }
         issue(tile + (NB - 1) * step, buf == 0 ? NB - 1 : buf - 1);
         if constexpr (pw_serial<CIN, NWV>()) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const char *sb = smem + buf * TILE_BYTES;
@@ -222,21 +238,18 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void pointwise_kernel(P
         // 16-byte stores (scattered 8-byte stores of 256-byte rows waste most of
         // each memory transaction).  Lane holds channels co0 + 8g + 4*(lane/32) + e
         // of voxel 32u + lane%32.
-        const int m0 = tile * BM;
         char *ob = obuf + wv * (BM * 64);  // this wave's [BM voxels][32 ch] fp16, row-swizzled
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const int co = co0 + 8 * g + 4 * rhi;
 #pragma unroll
             for (int u = 0; u < SUB; ++u) {
                 const int vrow = u * 32 + rrow;
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc[u][4 * g + e] + bv[g][e];
-                if (p.res && m0 + vrow < M) {
-                    const pw_half4 r4 = *reinterpret_cast<const pw_half4 *>(p.res + (int64_t)(m0 + vrow) * p.Cout + co);
+                if (p.res) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] += to_f32<E>(r4[e]);
+                    for (int e = 0; e < 4; ++e) v[e] += to_f32<E>(rv[u][g][e]);
                 }
                 pw_half4 h;
 #pragma unroll
