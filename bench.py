@@ -19,6 +19,7 @@ each roofline figure is also given as a fraction of those.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -153,7 +154,8 @@ def main():
                     help="wall seconds of oracle work for cpu_baseline (0 disables it)")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel extras")
     ap.add_argument("--extras", default="all",
-                    help="comma list of per-kernel extras to run: conv256, groupnorm, bf16, t1, stage "
+                    help="comma list of per-kernel extras to run: conv256, groupnorm, bf16, t1, t1zero "
+                         "(the zero-causal first frame), chunk (the block conv decoded in chunks), stage "
                          "(the 33-frame 256x256 3x3x3 and 1x1x1 pair), gemm (the vendor GEMM on the "
                          "headline's M x N x K, for context), or all")
     ap.add_argument("--no-calibration", action="store_true",
@@ -271,7 +273,7 @@ def main():
     result["decoder_block_config"] = ("GN(32, eps 1e-6)+SiLU -> causal conv3d 3x3x3 -> GN+SiLU -> "
                                       "causal conv3d 3x3x3 -> +x; N=1 C=256 T=17 H=W=128 fp16")
 
-    extras = ({"conv256", "groupnorm", "bf16", "t1", "stage", "gemm"} if args.extras == "all"
+    extras = ({"conv256", "groupnorm", "bf16", "t1", "t1zero", "chunk", "stage", "gemm"} if args.extras == "all"
               else set(args.extras.split(",")))
     if not args.no_kernels:
         kern = {}
@@ -340,6 +342,51 @@ def main():
                                         "TFLOP/s_folded": round(pt1.info().flops / t / 1e9, 1),
                                         "path": int(pt1.info().path)}
         del x1, y1, ws1
+
+    if not args.no_kernels and "t1zero" in extras:
+        # the zero-causal first frame: only the last temporal tap sees data
+        s1z = dataclasses.replace(workloads.CAUSAL_256_T1, tmode=workloads.TPAD_ZERO)
+        ptz = c3d.conv3d_plan(desc_of(c3d, s1z, c3d.CONV3D_F_BIAS))
+        wsz = ws_for(ptz, torch, dev)
+        xz = bx[:, :1].contiguous()
+        yz = torch.empty(out_dims(s1z), dtype=torch.float16, device=dev)
+
+        def t1z():
+            c3d.conv3d_forward(ptz, xz, bt["w1"], bt["b1"], None, yz, wsz)
+        _, p = time_steps(t1z, 20, 3, torch)
+        t = sum(p) / len(p)
+        kern["first_frame_zero_causal_256"] = {"us": round(t * 1e3, 2),
+                                               "TFLOP/s_one_tap": round(ptz.info().flops / t / 1e9, 1),
+                                               "path": int(ptz.info().path)}
+        del xz, yz, wsz
+
+    if not args.no_kernels and "chunk" in extras:
+        # the 17-frame block conv decoded as chunks of 5, 4, 4 and 4 frames: the
+        # first with the causal plan, each later one with the previous chunk's
+        # last two input frames as history (the same output as the whole conv)
+        sizes = [5, 4, 4, 4]
+        cplans, t0 = [], 0
+        for k, tc in enumerate(sizes):
+            sc = dataclasses.replace(s4, t=tc)
+            fl = c3d.CONV3D_F_BIAS | (c3d.CONV3D_F_CHUNK if k else 0)
+            pc = c3d.conv3d_plan(desc_of(c3d, sc, fl))
+            cplans.append((pc, ws_for(pc, torch, dev), t0, tc))
+            t0 += tc
+
+        def chunked():
+            for k, (pc, wsc, a, tc) in enumerate(cplans):
+                if k == 0:
+                    c3d.conv3d_forward(pc, bx[:, a:a + tc], bt["w1"], bt["b1"], None, c1[:, a:a + tc], wsc)
+                else:
+                    c3d.conv3d_forward_chunk(pc, bx[:, a - 2:a], bx[:, a:a + tc], bt["w1"], bt["b1"], None,
+                                             c1[:, a:a + tc], wsc)
+        _, p = time_steps(chunked, 10, 2, torch)
+        t = sum(p) / len(p)
+        kern["chunked_causal_conv_256_T17_as_5_4_4_4"] = {
+            "ms": round(t, 4), "TFLOP/s": round(conv_flops / t / 1e9, 1),
+            "ms_over_whole_conv": round(t / kern["causal_conv_256_T17"]["ms"], 3)
+            if "causal_conv_256_T17" in kern else None}
+        del cplans
     del a1, c1, a2, out, bx
 
     if not args.no_kernels and "gemm" in extras:

@@ -95,6 +95,7 @@ constexpr double kBestRatePerCU = 1220e12 / kCUs;  // flop/s of the best tile co
 constexpr double kFixupBytesPerSec = 4.5e12;
 constexpr double kLaunchSeconds = 4e-6;
 constexpr size_t kMaxSplitWorkspace = (size_t)256 << 20;
+constexpr double kCopyBytesPerSec = 5.5e12;  // device-to-device copy, read + write bytes
 
 // Cost model: each CU runs ceil(tiles/CUs) whole tiles at the configuration's
 // measured rate; a split run fills the last wave with K-pieces instead and
@@ -136,15 +137,20 @@ struct conv3d_plan_s {
     size_t ws_bytes;
     int64_t x_elems, w_elems, y_elems;
     double flops;
-    // chunked causal decoding (CONV3D_F_CHUNK): per sample, a head conv over
-    // [x_prev; the first frames of x] copied into the workspace gives the
-    // first head_out output frames, and a conv over x without temporal padding
-    // (main, absent when x is too short) gives the rest
+    double est_seconds = 0.0;  // the cost model's time for the chosen decomposition
+    // chunked causal decoding (CONV3D_F_CHUNK), per sample, one of two ways:
+    //  * cat: [x_prev; x] copied into the workspace, one conv over it without
+    //    temporal padding;
+    //  * split: a head conv over [x_prev; the first frames of x] copied into
+    //    the workspace gives the first head_out output frames, and a conv over
+    //    x without temporal padding (main, absent when x is too short) gives
+    //    the rest.
     bool chunk = false;
-    conv3d_plan_s *head = nullptr, *main = nullptr;
+    conv3d_plan_s *cat = nullptr, *head = nullptr, *main = nullptr;
     int head_t = 0, head_out = 0;
-    size_t head_in_bytes = 0;  // 256-aligned; the sub-plans' workspace follows
+    size_t head_in_bytes = 0;  // 256-aligned copy of the conv input; the sub-plans' workspace follows
     ~conv3d_plan_s() {
+        delete cat;
         delete head;
         delete main;
     }
@@ -302,6 +308,7 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
     q.partial = nullptr;
     p->ws_bytes = p->ws_fold + (size_t)q.sk_tiles * q.sk_pieces * best->bm * best->bn * 4;
     p->flops = 2.0 * (double)q.M * q.Cout * q.K;
+    p->est_seconds = best_d.seconds + kLaunchSeconds;
     p->streaming = path == CONV3D_PATH_POINTWISE && c3d::pointwise_supported(q.Cin, q.Cout) &&
                    !(forced && *forced);
     if (p->streaming) {  // the streaming kernel neither splits K nor needs a workspace
@@ -318,8 +325,8 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
 conv3d_status conv3d_plan_query(conv3d_plan_t p, conv3d_plan_info *info) {
     if (!p || !info) return fail(CONV3D_ERR_INVALID_ARG, "null argument");
     memset(info, 0, sizeof(*info));
-    if (p->chunk) {  // the main conv's kernel, with the whole chunk's GEMM and work
-        const conv3d_status st = conv3d_plan_query(p->main ? p->main : p->head, info);
+    if (p->chunk) {  // the (main) conv's kernel, with the whole chunk's GEMM and work
+        const conv3d_status st = conv3d_plan_query(p->cat ? p->cat : (p->main ? p->main : p->head), info);
         if (st != CONV3D_OK) return st;
         info->t_out = p->d.t;
         info->gemm_m = (int64_t)p->d.n * p->d.t * info->h_out * info->w_out;
@@ -468,11 +475,17 @@ conv3d_status conv3d_forward_chunk(conv3d_plan_t p, const void *x_prev, const vo
         const char *x_n = static_cast<const char *>(x) + frame_in * d.t * n;
         char *y_n = static_cast<char *>(y) + frame_out * d.t * n;
         const char *r_n = has_res ? static_cast<const char *>(residual) + frame_out * d.t * n : nullptr;
-        // head input: the history, then the first frames of this chunk
+        // conv input: the history, then this chunk (cat) or its first frames (head)
         hipError_t e = hipMemcpyAsync(hin, xp_n, frame_in * ptf, hipMemcpyDeviceToDevice, s);
         if (e == hipSuccess)
-            e = hipMemcpyAsync(hin + frame_in * ptf, x_n, frame_in * (p->head_t - ptf), hipMemcpyDeviceToDevice, s);
-        if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "chunk head copy: %s", hipGetErrorString(e));
+            e = hipMemcpyAsync(hin + frame_in * ptf, x_n, frame_in * (p->cat ? d.t : p->head_t - ptf),
+                               hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "chunk input copy: %s", hipGetErrorString(e));
+        if (p->cat) {
+            st = conv3d_forward(p->cat, hin, weight, bias, r_n, y_n, sub_ws, sub_bytes, stream);
+            if (st != CONV3D_OK) return st;
+            continue;
+        }
         st = conv3d_forward(p->head, hin, weight, bias, r_n, y_n, sub_ws, sub_bytes, stream);
         if (st != CONV3D_OK) return st;
         if (p->main) {
@@ -564,11 +577,13 @@ conv3d_status conv3d_calibrate_hbm(const void *src, void *dst, size_t bytes, dou
 }
 
 // CONV3D_F_CHUNK: output frame t of a chunk reads frames t-kt+1 .. t, the
-// negative ones from x_prev (the previous chunk's last kt-1 frames).  Output
-// frames 0 .. min(T, kt-1)-1 come from a head conv over [x_prev; x frames
-// 0 .. min(T, kt-1)-1] and the rest from the chunk alone; both without
-// temporal padding, one sample at a time (the sub-convs' outputs are frame
-// ranges of each sample).
+// negative ones from x_prev (the previous chunk's last kt-1 frames).  One
+// sample at a time, without temporal padding, either one conv over a copy of
+// [x_prev; x] (cat), or a head conv over a copy of [x_prev; x frames
+// 0 .. min(T, kt-1)-1] for the first output frames and a conv over x alone for
+// the rest (split).  cat copies more; split runs two launches, each rounded up
+// to whole waves of tiles.  The cost model picks (CONV3D_CHUNK=cat or split
+// forces one).
 static conv3d_status plan_chunk(const conv3d_desc *d, conv3d_plan_t *out, size_t *workspace_bytes) {
     if (d->kt < 2 || d->pad_t_front != d->kt - 1 || d->pad_t_back != 0)
         return fail(CONV3D_ERR_INVALID_ARG, "CONV3D_F_CHUNK needs kt > 1, pad_t_front = kt-1 and pad_t_back = 0");
@@ -599,19 +614,44 @@ static conv3d_status plan_chunk(const conv3d_desc *d, conv3d_plan_t *out, size_t
     sub.pad_t_back = 0;
     sub.t_pad_mode = CONV3D_TPAD_ZERO;
     sub.t = p->head_t;
-    size_t ws_head = 0, ws_main = 0;
+    size_t ws_head = 0, ws_main = 0, ws_cat = 0;
     st = conv3d_plan(&sub, &p->head, &ws_head);
     if (st == CONV3D_OK && d->t > hist) {
         sub.t = d->t;
         st = conv3d_plan(&sub, &p->main, &ws_main);
     }
+    if (st == CONV3D_OK && p->main) {
+        sub.t = hist + d->t;
+        st = conv3d_plan(&sub, &p->cat, &ws_cat);
+    }
     if (st != CONV3D_OK) {
         delete p;
         return st;
     }
-    p->head_in_bytes = ((size_t)p->head_t * d->h * d->w * d->c_in * 2 + 255) & ~(size_t)255;
-    p->ws_bytes = p->head_in_bytes + (ws_head > ws_main ? ws_head : ws_main);
-    p->flops = (double)d->n * (p->head->flops + (p->main ? p->main->flops : 0.0));
+    const size_t frame_in = (size_t)d->h * d->w * d->c_in * 2;
+    if (p->cat) {
+        // copies count their read and write; the cost model's times already
+        // include a launch each
+        const double split_s = p->head->est_seconds + p->main->est_seconds + 2.0 * p->head_t * frame_in / kCopyBytesPerSec;
+        const double cat_s = p->cat->est_seconds + 2.0 * (hist + d->t) * frame_in / kCopyBytesPerSec;
+        const char *force = getenv("CONV3D_CHUNK");
+        const bool use_cat = force && strcmp(force, "cat") == 0 ? true
+                             : force && strcmp(force, "split") == 0 ? false
+                                                                     : cat_s < split_s;
+        if (use_cat) {
+            delete p->head;
+            delete p->main;
+            p->head = p->main = nullptr;
+        } else {
+            delete p->cat;
+            p->cat = nullptr;
+        }
+    }
+    const int copied = p->cat ? hist + d->t : p->head_t;
+    p->head_in_bytes = ((size_t)copied * frame_in + 255) & ~(size_t)255;
+    const size_t ws_sub = p->cat ? ws_cat : (ws_head > ws_main ? ws_head : ws_main);
+    p->ws_bytes = p->head_in_bytes + ws_sub;
+    p->flops = (double)d->n * (p->cat ? p->cat->flops : p->head->flops + (p->main ? p->main->flops : 0.0));
     p->path = CONV3D_PATH_GENERAL;
     *out = p;
     *workspace_bytes = p->ws_bytes;

@@ -269,6 +269,38 @@ def test_chunk_plans_and_argument_checks():
     assert fc(p, wsb=16) == c3d.CONV3D_ERR_WORKSPACE
 
 
+def test_chunk_strategies_and_their_workspace():
+    # one conv over a copy of [x_prev; x] ("cat") copies kt-1 + t frames; a head
+    # conv plus a conv over x alone ("split") copies kt-1 + min(t, kt-1)
+    ch = c3d.CONV3D_F_CHUNK | c3d.CONV3D_F_BIAS
+    d = desc(flags=ch, t=4, h=128, w=128, c_in=256, c_out=256)
+    frame = 128 * 128 * 256 * 2
+
+    def plan(strategy):
+        old = os.environ.get("CONV3D_CHUNK")
+        if strategy is None:
+            os.environ.pop("CONV3D_CHUNK", None)
+        else:
+            os.environ["CONV3D_CHUNK"] = strategy
+        try:
+            return c3d.conv3d_plan(d)
+        finally:
+            if old is None:
+                os.environ.pop("CONV3D_CHUNK", None)
+            else:
+                os.environ["CONV3D_CHUNK"] = old
+    cat, split, auto = plan("cat"), plan("split"), plan(None)
+    assert cat.workspace_bytes >= (2 + 4) * frame and split.workspace_bytes >= (2 + 2) * frame
+    for p in (cat, split, auto):
+        i = p.info()
+        assert i.t_out == 4 and i.gemm_m == 4 * 128 * 128 and i.flops == cat.info().flops
+    # two output frames per launch are half a wave of 256x256 tiles on 256 CUs:
+    # the cost model runs the 4-frame chunk as one conv
+    assert auto.workspace_bytes == cat.workspace_bytes
+    # a chunk no longer than the history is one head conv either way
+    assert plan("cat").info().t_out == 4 and c3d.conv3d_plan(desc(flags=ch, t=2)).info().t_out == 2
+
+
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="host without a GPU only")
 def test_chunk_without_a_device_reports_no_device():
     lib = c3d.load_library()

@@ -4,6 +4,9 @@ A chunk's output is the conv of [x_prev; x] along t with no temporal padding,
 so the oracle is conv3d over that concatenation (pads (0, 0, ph, pw)).  Decoding
 a video in chunks must also reproduce the whole-video causal conv: with ternary
 data every sum is exact, so the two agree bit for bit whatever the tiling.
+Both ways of running a chunk are checked: one conv over a copy of the
+concatenation ("cat") and a head conv plus a conv over the chunk alone
+("split"), forced through CONV3D_CHUNK, next to the planner's own choice.
 """
 import numpy as np
 import pytest
@@ -14,16 +17,20 @@ import oracle
 import workloads
 from workloads import ConvShape, TPAD_REPLICATE as R, TPAD_ZERO as Z
 
-from helpers import (assert_conv_close, check_guards, conv_desc, dev, guarded_empty, host_bits, out_dims,
-                     run_conv, ulp_bf16, workspace_for)
+from helpers import (assert_conv_close, check_guards, conv_desc, dev, env_var, guarded_empty, host_bits,
+                     out_dims, run_conv, ulp_bf16, workspace_for)
 
 pytestmark = pytest.mark.gpu
 
 
-def chunk(shape, x_prev, x, w, b=None, res=None, bf16=False):
+STRATEGIES = [None, "cat", "split"]
+
+
+def chunk(shape, x_prev, x, w, b=None, res=None, bf16=False, strategy=None):
     flags = c3d.CONV3D_F_CHUNK | (c3d.CONV3D_F_BIAS if b is not None else 0) | \
         (c3d.CONV3D_F_RESIDUAL if res is not None else 0) | (c3d.CONV3D_F_BF16 if bf16 else 0)
-    plan = c3d.conv3d_plan(conv_desc(shape, flags))
+    with env_var("CONV3D_CHUNK", strategy):
+        plan = c3d.conv3d_plan(conv_desc(shape, flags))
     buf, y = guarded_empty(out_dims(shape), torch.bfloat16 if bf16 else torch.float16)
     ws = workspace_for(plan)
     c3d.conv3d_forward_chunk(plan, dev(x_prev), dev(x), dev(w), None if b is None else dev(b),
@@ -53,19 +60,21 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("strategy", STRATEGIES)
 @pytest.mark.parametrize("case", range(len(CASES)))
-def test_chunk_matches_conv_of_the_concatenation(case):
+def test_chunk_matches_conv_of_the_concatenation(case, strategy):
     s = CASES[case]
     d = workloads.conv_inputs(s, 900 + case)
     x_prev = workloads.normal_f16(np.random.SeedSequence(950 + case), (s.n, s.kt - 1, s.h, s.w, s.cin))
     res = workloads.normal_f16(np.random.SeedSequence(960 + case), out_dims(s))
-    y = chunk(s, x_prev, d["x"], d["w"], d["b"], res)
+    y = chunk(s, x_prev, d["x"], d["w"], d["b"], res, strategy=strategy)
     ref, mag = concat_oracle(s, x_prev, d["x"], d["w"], d["b"], res)
     assert_conv_close(y, ref, mag, "chunk " + str(s))
 
 
+@pytest.mark.parametrize("strategy", STRATEGIES)
 @pytest.mark.parametrize("n,tc", [(1, 6), (2, 3), (1, 1)])
-def test_chunked_decode_equals_whole_video_decode(n, tc):
+def test_chunked_decode_equals_whole_video_decode(n, tc, strategy):
     # a video of 3 chunks of tc frames: chunk 0 with the causal (replicate)
     # plan, chunks 1 and 2 with their predecessor's last 2 frames as history
     whole = ConvShape(n, 3 * tc, 10, 12, 64, 56, tmode=R)
@@ -81,7 +90,8 @@ def test_chunked_decode_equals_whole_video_decode(n, tc):
         # chunk k's history: frames k*tc-2 and k*tc-1, clamped at 0 as the
         # whole video's replicate padding clamps them
         hist = [max(k * tc - 2, 0), max(k * tc - 1, 0)]
-        parts.append(chunk(part, np.ascontiguousarray(x[:, hist]), x[:, k * tc:(k + 1) * tc], w, b))
+        parts.append(chunk(part, np.ascontiguousarray(x[:, hist]), x[:, k * tc:(k + 1) * tc], w, b,
+                           strategy=strategy))
     assert np.array_equal(np.concatenate(parts, axis=1), y_whole)
 
 
