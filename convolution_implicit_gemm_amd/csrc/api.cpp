@@ -96,6 +96,7 @@ constexpr double kFixupBytesPerSec = 4.5e12;
 constexpr double kLaunchSeconds = 4e-6;
 constexpr size_t kMaxSplitWorkspace = (size_t)256 << 20;
 constexpr double kCopyBytesPerSec = 5.5e12;  // device-to-device copy, read + write bytes
+constexpr size_t kMaxChunkCopy = (size_t)512 << 20;  // largest [x_prev; x] copy a chunk plan makes
 
 // Cost model: each CU runs ceil(tiles/CUs) whole tiles at the configuration's
 // measured rate; a split run fills the last wave with K-pieces instead and
@@ -620,15 +621,17 @@ static conv3d_status plan_chunk(const conv3d_desc *d, conv3d_plan_t *out, size_t
         sub.t = d->t;
         st = conv3d_plan(&sub, &p->main, &ws_main);
     }
-    if (st == CONV3D_OK && p->main) {
+    const size_t frame_in = (size_t)d->h * d->w * d->c_in * 2;
+    if (st == CONV3D_OK && p->main && (size_t)(hist + d->t) * frame_in <= kMaxChunkCopy) {
+        // one conv over the whole copy: an option only; when it cannot be
+        // planned, the two convs above run the chunk
         sub.t = hist + d->t;
-        st = conv3d_plan(&sub, &p->cat, &ws_cat);
+        if (conv3d_plan(&sub, &p->cat, &ws_cat) != CONV3D_OK) p->cat = nullptr;
     }
     if (st != CONV3D_OK) {
         delete p;
         return st;
     }
-    const size_t frame_in = (size_t)d->h * d->w * d->c_in * 2;
     if (p->cat) {
         // copies count their read and write; the cost model's times already
         // include a launch each

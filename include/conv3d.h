@@ -168,8 +168,9 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
  * copies x_prev and all of x into the workspace and runs one conv over the
  * copy, or copies x_prev and the first min(t, kt-1) frames of x and runs two
  * convs (that head, then x alone); the plan picks the cheaper by its cost model
- * (the environment variable CONV3D_CHUNK=cat or =split forces one) and sizes
- * the workspace for it.  A CONV3D_F_CHUNK plan is rejected
+ * (the environment variable CONV3D_CHUNK=cat or =split forces one; the first
+ * is only an option while a sample's copy stays within 512 MiB) and sizes the
+ * workspace for it.  A CONV3D_F_CHUNK plan is rejected
  * by conv3d_forward and vice versa.  Errors as conv3d_forward, plus
  * INVALID_ARG for a null x_prev or y overlapping it.
  */

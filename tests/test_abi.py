@@ -299,6 +299,10 @@ def test_chunk_strategies_and_their_workspace():
     assert auto.workspace_bytes == cat.workspace_bytes
     # a chunk no longer than the history is one head conv either way
     assert plan("cat").info().t_out == 4 and c3d.conv3d_plan(desc(flags=ch, t=2)).info().t_out == 2
+    # a copy of [x_prev; x] beyond 512 MiB per sample is not an option, even when asked for
+    d = desc(flags=ch, t=40, h=128, w=128, c_in=512, c_out=256)
+    big_cat, big_split = plan("cat"), plan("split")
+    assert big_cat.workspace_bytes == big_split.workspace_bytes < (2 + 2 + 1) * 128 * 128 * 512 * 2 + (256 << 20)
 
 
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="host without a GPU only")
