@@ -139,13 +139,13 @@ struct conv3d_plan_s {
     int64_t x_elems, w_elems, y_elems;
     double flops;
     double est_seconds = 0.0;  // the cost model's time for the chosen decomposition
-    // chunked causal decoding (CONV3D_F_CHUNK), per sample, one of two ways:
-    //  * cat: [x_prev; x] copied into the workspace, one conv over it without
-    //    temporal padding;
-    //  * split: a head conv over [x_prev; the first frames of x] copied into
-    //    the workspace gives the first head_out output frames, and a conv over
-    //    x without temporal padding (main, absent when x is too short) gives
-    //    the rest.
+    // chunked causal decoding (CONV3D_F_CHUNK), one of two ways:
+    //  * cat: [x_prev; x] of every sample copied into the workspace, one conv
+    //    over all of it without temporal padding;
+    //  * split, per sample: a head conv over [x_prev; the first frames of x]
+    //    copied into the workspace gives the first head_out output frames, and
+    //    a conv over x without temporal padding (main, absent when x is too
+    //    short) gives the rest.
     bool chunk = false;
     conv3d_plan_s *cat = nullptr, *head = nullptr, *main = nullptr;
     int head_t = 0, head_out = 0;
@@ -476,15 +476,18 @@ conv3d_status conv3d_forward_chunk(conv3d_plan_t p, const void *x_prev, const vo
         const char *x_n = static_cast<const char *>(x) + frame_in * d.t * n;
         char *y_n = static_cast<char *>(y) + frame_out * d.t * n;
         const char *r_n = has_res ? static_cast<const char *>(residual) + frame_out * d.t * n : nullptr;
-        // conv input: the history, then this chunk (cat) or its first frames (head)
-        hipError_t e = hipMemcpyAsync(hin, xp_n, frame_in * ptf, hipMemcpyDeviceToDevice, s);
+        // conv input: the history, then this chunk (cat: every sample, one
+        // after the other) or its first frames (head)
+        char *in_n = p->cat ? hin + frame_in * (ptf + d.t) * n : hin;
+        hipError_t e = hipMemcpyAsync(in_n, xp_n, frame_in * ptf, hipMemcpyDeviceToDevice, s);
         if (e == hipSuccess)
-            e = hipMemcpyAsync(hin + frame_in * ptf, x_n, frame_in * (p->cat ? d.t : p->head_t - ptf),
+            e = hipMemcpyAsync(in_n + frame_in * ptf, x_n, frame_in * (p->cat ? d.t : p->head_t - ptf),
                                hipMemcpyDeviceToDevice, s);
         if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "chunk input copy: %s", hipGetErrorString(e));
         if (p->cat) {
-            st = conv3d_forward(p->cat, hin, weight, bias, r_n, y_n, sub_ws, sub_bytes, stream);
-            if (st != CONV3D_OK) return st;
+            if (n + 1 == d.n)
+                return conv3d_forward(p->cat, hin, weight, bias, has_res ? residual : nullptr, y, sub_ws, sub_bytes,
+                                      stream);
             continue;
         }
         st = conv3d_forward(p->head, hin, weight, bias, r_n, y_n, sub_ws, sub_bytes, stream);
@@ -578,9 +581,9 @@ conv3d_status conv3d_calibrate_hbm(const void *src, void *dst, size_t bytes, dou
 }
 
 // CONV3D_F_CHUNK: output frame t of a chunk reads frames t-kt+1 .. t, the
-// negative ones from x_prev (the previous chunk's last kt-1 frames).  One
-// sample at a time, without temporal padding, either one conv over a copy of
-// [x_prev; x] (cat), or a head conv over a copy of [x_prev; x frames
+// negative ones from x_prev (the previous chunk's last kt-1 frames).  Without
+// temporal padding, either one conv over a copy of [x_prev; x] of every sample
+// (cat), or per sample a head conv over a copy of [x_prev; x frames
 // 0 .. min(T, kt-1)-1] for the first output frames and a conv over x alone for
 // the rest (split).  cat copies more; split runs two launches, each rounded up
 // to whole waves of tiles.  The cost model picks (CONV3D_CHUNK=cat or split
@@ -622,10 +625,11 @@ static conv3d_status plan_chunk(const conv3d_desc *d, conv3d_plan_t *out, size_t
         st = conv3d_plan(&sub, &p->main, &ws_main);
     }
     const size_t frame_in = (size_t)d->h * d->w * d->c_in * 2;
-    if (st == CONV3D_OK && p->main && (size_t)(hist + d->t) * frame_in <= kMaxChunkCopy) {
-        // one conv over the whole copy: an option only; when it cannot be
-        // planned, the two convs above run the chunk
+    if (st == CONV3D_OK && p->main && (size_t)d->n * (hist + d->t) * frame_in <= kMaxChunkCopy) {
+        // one conv over the copy of every sample: an option only; when it
+        // cannot be planned, the two convs above run the chunk
         sub.t = hist + d->t;
+        sub.n = d->n;
         if (conv3d_plan(&sub, &p->cat, &ws_cat) != CONV3D_OK) p->cat = nullptr;
     }
     if (st != CONV3D_OK) {
@@ -635,8 +639,9 @@ static conv3d_status plan_chunk(const conv3d_desc *d, conv3d_plan_t *out, size_t
     if (p->cat) {
         // copies count their read and write; the cost model's times already
         // include a launch each
-        const double split_s = p->head->est_seconds + p->main->est_seconds + 2.0 * p->head_t * frame_in / kCopyBytesPerSec;
-        const double cat_s = p->cat->est_seconds + 2.0 * (hist + d->t) * frame_in / kCopyBytesPerSec;
+        const double split_s =
+            d->n * (p->head->est_seconds + p->main->est_seconds + 2.0 * p->head_t * frame_in / kCopyBytesPerSec);
+        const double cat_s = p->cat->est_seconds + 2.0 * d->n * (hist + d->t) * frame_in / kCopyBytesPerSec;
         const char *force = getenv("CONV3D_CHUNK");
         const bool use_cat = force && strcmp(force, "cat") == 0 ? true
                              : force && strcmp(force, "split") == 0 ? false
@@ -650,11 +655,11 @@ static conv3d_status plan_chunk(const conv3d_desc *d, conv3d_plan_t *out, size_t
             p->cat = nullptr;
         }
     }
-    const int copied = p->cat ? hist + d->t : p->head_t;
+    const int copied = p->cat ? d->n * (hist + d->t) : p->head_t;
     p->head_in_bytes = ((size_t)copied * frame_in + 255) & ~(size_t)255;
     const size_t ws_sub = p->cat ? ws_cat : (ws_head > ws_main ? ws_head : ws_main);
     p->ws_bytes = p->head_in_bytes + ws_sub;
-    p->flops = (double)d->n * (p->cat ? p->cat->flops : p->head->flops + (p->main ? p->main->flops : 0.0));
+    p->flops = p->cat ? p->cat->flops : (double)d->n * (p->head->flops + (p->main ? p->main->flops : 0.0));
     p->path = CONV3D_PATH_GENERAL;
     *out = p;
     *workspace_bytes = p->ws_bytes;

@@ -164,13 +164,13 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
  * y equals the conv of [x_prev; x] along t with no temporal padding.  Decoding
  * a video chunk by chunk (the first chunk with the ordinary causal plan, the
  * next ones with x_prev = the last kt-1 frames of the previous chunk's input)
- * therefore gives the same outputs as decoding it whole.  Per sample it either
- * copies x_prev and all of x into the workspace and runs one conv over the
- * copy, or copies x_prev and the first min(t, kt-1) frames of x and runs two
- * convs (that head, then x alone); the plan picks the cheaper by its cost model
- * (the environment variable CONV3D_CHUNK=cat or =split forces one; the first
- * is only an option while a sample's copy stays within 512 MiB) and sizes the
- * workspace for it.  A CONV3D_F_CHUNK plan is rejected
+ * therefore gives the same outputs as decoding it whole.  It either copies
+ * x_prev and x of every sample into the workspace and runs one conv over the
+ * copy, or, per sample, copies x_prev and the first min(t, kt-1) frames of x
+ * and runs two convs (that head, then x alone); the plan picks the cheaper by
+ * its cost model (the environment variable CONV3D_CHUNK=cat or =split forces
+ * one; the first is only an option while the copy stays within 512 MiB) and
+ * sizes the workspace for it.  A CONV3D_F_CHUNK plan is rejected
  * by conv3d_forward and vice versa.  Errors as conv3d_forward, plus
  * INVALID_ARG for a null x_prev or y overlapping it.
  */
