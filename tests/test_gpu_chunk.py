@@ -95,10 +95,11 @@ def test_chunked_decode_equals_whole_video_decode(n, tc, strategy):
     assert np.array_equal(np.concatenate(parts, axis=1), y_whole)
 
 
-def test_chunk_bf16():
+@pytest.mark.parametrize("strategy", STRATEGIES)
+def test_chunk_bf16(strategy):
     s = ConvShape(2, 4, 12, 10, 64, 64)
     d = workloads.conv_inputs(s, 990, dtype="bf16")
     x_prev = workloads.normal_f16(np.random.SeedSequence(991), (s.n, 2, s.h, s.w, s.cin), dtype="bf16")
-    y = chunk(s, x_prev, d["x"], d["w"], d["b"], bf16=True)
+    y = chunk(s, x_prev, d["x"], d["w"], d["b"], bf16=True, strategy=strategy)
     ref, mag = concat_oracle(s, x_prev, d["x"], d["w"], d["b"], dec=oracle.bf16_to_f64)
     assert_conv_close(oracle.bf16_to_f64(y), ref, mag, "bf16 chunk", ulp=ulp_bf16)

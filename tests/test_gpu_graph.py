@@ -88,9 +88,11 @@ def test_decoder_block_graph_replays_equal_eager():
             assert torch.equal(bits(getattr(graphed, name)), bits(getattr(eager, name))), (k, name)
 
 
-def test_chunked_forward_graph_replays_equal_eager():
+@pytest.mark.parametrize("strategy", ["cat", "split"])
+def test_chunked_forward_graph_replays_equal_eager(strategy):
     s = ConvShape(2, 4, 12, 10, 64, 64)
-    plan = c3d.conv3d_plan(conv_desc(s, c3d.CONV3D_F_BIAS | c3d.CONV3D_F_CHUNK))
+    with env_var("CONV3D_CHUNK", strategy):
+        plan = c3d.conv3d_plan(conv_desc(s, c3d.CONV3D_F_BIAS | c3d.CONV3D_F_CHUNK))
     d = workloads.conv_inputs(s, 1520)
     w, b = dev(d["w"]), dev(d["b"])
     hist_shape = (s.n, s.kt - 1, s.h, s.w, s.cin)
