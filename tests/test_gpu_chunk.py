@@ -53,6 +53,8 @@ def concat_oracle(shape, x_prev, x, w, b=None, res=None, dec=widen):
 
 CASES = [
     ConvShape(1, 5, 12, 14, 64, 64),
+    ConvShape(1, 6, 9, 11, 48, 64, kt=5, pad_t_front=4, pad_t_back=0),   # four history frames (general gather)
+    ConvShape(2, 3, 8, 10, 64, 32, kt=2, kh=1, kw=1, pad_t_front=1, pad_t_back=0, pad_h=0, pad_w=0),  # one history frame, 2x1x1 kernel
     ConvShape(2, 4, 9, 10, 40, 48),            # channel tail, two samples
     ConvShape(1, 1, 16, 16, 128, 64),          # one frame: the head conv alone
     ConvShape(1, 2, 8, 8, 32, 32),             # as long as the history: head conv alone
