@@ -39,7 +39,8 @@ EXPORTED = ("conv3d_plan", "conv3d_plan_query", "conv3d_plan_destroy", "conv3d_f
             "conv3d_forward_chunk",
             "groupnorm_silu_workspace", "groupnorm_silu", "groupnorm_silu_bf16",
             "conv3d_calibrate_scratch_bytes",
-            "conv3d_calibrate_mfma", "conv3d_calibrate_hbm", "conv3d_status_str",
+            "conv3d_calibrate_mfma", "conv3d_calibrate_hbm", "conv3d_clock_stamp_bytes",
+            "conv3d_clock_stamp", "conv3d_status_str",
             "conv3d_last_error", "conv3d_version", "conv3d_selftest")
 
 
@@ -115,6 +116,10 @@ def load_library(path: str = LIB_PATH):
     lib.conv3d_calibrate_mfma.restype = ctypes.c_int
     lib.conv3d_calibrate_hbm.argtypes = [vp, vp, sz, dp, dp, vp]
     lib.conv3d_calibrate_hbm.restype = ctypes.c_int
+    lib.conv3d_clock_stamp_bytes.argtypes = []
+    lib.conv3d_clock_stamp_bytes.restype = sz
+    lib.conv3d_clock_stamp.argtypes = [vp, sz, vp]
+    lib.conv3d_clock_stamp.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -124,12 +129,42 @@ def _check(status):
         raise Conv3dError(status, load_library().conv3d_last_error().decode())
 
 
-def _addr(t):
+def _addr(t, what="tensor", elems=None, dtype=None):
+    """Device address of a torch tensor (or an int address, passed as is).
+
+    A tensor must be contiguous and on a GPU; with ``elems`` / ``dtype`` it
+    must also hold at least that many elements of that dtype (the C layer
+    sees only the address and cannot check any of this).  Raises Conv3dError
+    (INVALID_ARG) otherwise, before anything is enqueued.
+    """
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_contiguous():
+        raise Conv3dError(CONV3D_ERR_INVALID_ARG, "%s is not contiguous (pass .contiguous())" % what)
+    if t.device.type != "cuda":
+        raise Conv3dError(CONV3D_ERR_INVALID_ARG, "%s is on %s, not on a GPU" % (what, t.device))
+    if dtype is not None and t.dtype != dtype:
+        raise Conv3dError(CONV3D_ERR_INVALID_ARG, "%s is %s, the plan expects %s" % (what, t.dtype, dtype))
+    if elems is not None and t.numel() < elems:
+        raise Conv3dError(CONV3D_ERR_INVALID_ARG, "%s holds %d elements, %d needed" % (what, t.numel(), elems))
     return t.data_ptr()
+
+
+def _elem_dtype(bf16):
+    import torch
+    return torch.bfloat16 if bf16 else torch.float16
+
+
+def _conv_sizes(desc, chunk_t=None):
+    """(x, x_prev, weight, bias, y) element counts of a plan's descriptor."""
+    d = desc
+    to = d.t if chunk_t else d.t + d.pad_t_front + d.pad_t_back - d.kt + 1
+    ho = d.h + 2 * d.pad_h - d.kh + 1
+    wo = d.w + 2 * d.pad_w - d.kw + 1
+    return (d.n * d.t * d.h * d.w * d.c_in, d.n * max(d.kt - 1, 0) * d.h * d.w * d.c_in,
+            d.c_out * d.kt * d.kh * d.kw * d.c_in, d.c_out, d.n * to * ho * wo * d.c_out)
 
 
 def _stream(stream):
@@ -201,8 +236,11 @@ def conv3d_forward(plan: Plan, x, weight, bias, residual, y, workspace=None, wor
             workspace_bytes = plan.workspace_bytes
         else:
             workspace_bytes = workspace.numel() * workspace.element_size()
-    _check(load_library().conv3d_forward(plan.handle, _addr(x), _addr(weight), _addr(bias),
-                                         _addr(residual), _addr(y), _addr(workspace),
+    nx, _, nw, nb, ny = _conv_sizes(plan.desc)
+    dt = _elem_dtype(plan.desc.flags & CONV3D_F_BF16)
+    _check(load_library().conv3d_forward(plan.handle, _addr(x, "x", nx, dt), _addr(weight, "weight", nw, dt),
+                                         _addr(bias, "bias", nb, dt), _addr(residual, "residual", ny, dt),
+                                         _addr(y, "y", ny, dt), _addr(workspace, "workspace"),
                                          workspace_bytes, _stream(stream)))
 
 
@@ -211,8 +249,12 @@ def conv3d_forward_chunk(plan: Plan, x_prev, x, weight, bias, residual, y, works
     """Enqueue one chunk of a chunked causal decode (plan made with CONV3D_F_CHUNK)."""
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load_library().conv3d_forward_chunk(plan.handle, _addr(x_prev), _addr(x), _addr(weight),
-                                               _addr(bias), _addr(residual), _addr(y), _addr(workspace),
+    nx, nxp, nw, nb, ny = _conv_sizes(plan.desc, chunk_t=True)
+    dt = _elem_dtype(plan.desc.flags & CONV3D_F_BF16)
+    _check(load_library().conv3d_forward_chunk(plan.handle, _addr(x_prev, "x_prev", nxp, dt), _addr(x, "x", nx, dt),
+                                               _addr(weight, "weight", nw, dt), _addr(bias, "bias", nb, dt),
+                                               _addr(residual, "residual", ny, dt), _addr(y, "y", ny, dt),
+                                               _addr(workspace, "workspace"),
                                                workspace_bytes, _stream(stream)))
 
 
@@ -227,8 +269,10 @@ def groupnorm_silu(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, worksp
         workspace_bytes = workspace.numel() * workspace.element_size()
     lib = load_library()
     fn = lib.groupnorm_silu_bf16 if bf16 else lib.groupnorm_silu
-    _check(fn(_addr(x), _addr(gamma), _addr(beta), _addr(y), n, thw, c, groups, float(eps),
-              1 if apply_silu else 0, _addr(workspace), workspace_bytes, _stream(stream)))
+    dt, ne = _elem_dtype(bf16), n * thw * c
+    _check(fn(_addr(x, "x", ne, dt), _addr(gamma, "gamma", c, dt), _addr(beta, "beta", c, dt), _addr(y, "y", ne, dt),
+              n, thw, c, groups, float(eps), 1 if apply_silu else 0, _addr(workspace, "workspace"),
+              workspace_bytes, _stream(stream)))
 
 
 def conv3d_calibrate_scratch_bytes() -> int:
@@ -251,6 +295,33 @@ def conv3d_calibrate_hbm(src, dst, nbytes, stream=None):
     _check(load_library().conv3d_calibrate_hbm(_addr(src), _addr(dst), nbytes, ctypes.byref(rd),
                                                ctypes.byref(cp), _stream(stream)))
     return rd.value, cp.value
+
+
+def conv3d_clock_stamp_bytes() -> int:
+    return load_library().conv3d_clock_stamp_bytes()
+
+
+def conv3d_clock_stamp(out, out_bytes=None, stream=None) -> None:
+    """Enqueue a shader-clock stamp into device buffer ``out`` (see conv3d.h)."""
+    if out_bytes is None:
+        out_bytes = out.numel() * out.element_size()
+    _check(load_library().conv3d_clock_stamp(_addr(out), out_bytes, _stream(stream)))
+
+
+def sclk_between(before, after):
+    """Mean shader clock (MHz) per XCD between two stamps (host uint64 arrays
+    of conv3d_clock_stamp's layout): {xcd: MHz}."""
+    import numpy as np
+    b = np.asarray(before, dtype=np.uint64).reshape(-1, 3)
+    a = np.asarray(after, dtype=np.uint64).reshape(-1, 3)
+    out = {}
+    for x in sorted(set(b[:, 2].tolist()) & set(a[:, 2].tolist())):
+        bb, aa = b[b[:, 2] == x], a[a[:, 2] == x]
+        dc = aa[:, 0].astype(np.float64).mean() - bb[:, 0].astype(np.float64).mean()
+        dr = aa[:, 1].astype(np.float64).mean() - bb[:, 1].astype(np.float64).mean()
+        if dr > 0:
+            out[int(x)] = 100.0 * dc / dr
+    return out
 
 
 def groupnorm_silu_bf16(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, workspace,

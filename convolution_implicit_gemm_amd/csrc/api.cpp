@@ -507,9 +507,9 @@ size_t groupnorm_silu_workspace(int32_t n, int64_t thw, int32_t c, int32_t group
     return c3d::gn_workspace_bytes(n, thw, c, groups);
 }
 
-static conv3d_status gn_entry(const void *x, const void *gamma, const void *beta, void *y, int32_t n, int64_t thw,
-                              int32_t c, int32_t groups, float eps, int32_t apply_silu, void *workspace,
-                              size_t workspace_bytes, void *stream, bool bf16) {
+// Argument checks shared by the GroupNorm entry points (workspace aside).
+static conv3d_status gn_check(const void *x, const void *gamma, const void *beta, const void *y, int32_t n,
+                              int64_t thw, int32_t c, int32_t groups, float eps) {
     if (!x || !gamma || !beta || !y) return fail(CONV3D_ERR_INVALID_ARG, "x, gamma, beta and y are required");
     if (n < 1 || thw < 1 || c < 1 || groups < 1) return fail(CONV3D_ERR_INVALID_ARG, "sizes must be positive");
     if (c % groups) return fail(CONV3D_ERR_INVALID_ARG, "c (%d) is not a multiple of groups (%d)", c, groups);
@@ -517,16 +517,25 @@ static conv3d_status gn_entry(const void *x, const void *gamma, const void *beta
     if ((c / groups) % 8 || c > 8192)
         return fail(CONV3D_ERR_UNSUPPORTED, "channels per group must be a multiple of 8 and c <= 8192");
     if ((int64_t)n * thw >= ((int64_t)1 << 40)) return fail(CONV3D_ERR_UNSUPPORTED, "tensor too large");
-    if (misaligned(x) || misaligned(y) || misaligned(workspace) || (reinterpret_cast<uintptr_t>(gamma) & 1) ||
+    if (misaligned(x) || misaligned(y) || (reinterpret_cast<uintptr_t>(gamma) & 1) ||
         (reinterpret_cast<uintptr_t>(beta) & 1))
-        return fail(CONV3D_ERR_INVALID_ARG, "x, y and workspace must be 16-byte aligned");
+        return fail(CONV3D_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
     const size_t bytes = (size_t)n * thw * c * 2;
     if (x != y && overlap(x, bytes, y, bytes)) return fail(CONV3D_ERR_INVALID_ARG, "x and y partially overlap");
+    return CONV3D_OK;
+}
+
+static conv3d_status gn_entry(const void *x, const void *gamma, const void *beta, void *y, int32_t n, int64_t thw,
+                              int32_t c, int32_t groups, float eps, int32_t apply_silu, void *workspace,
+                              size_t workspace_bytes, void *stream, bool bf16) {
+    conv3d_status st = gn_check(x, gamma, beta, y, n, thw, c, groups, eps);
+    if (st != CONV3D_OK) return st;
+    if (misaligned(workspace)) return fail(CONV3D_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     const size_t need = c3d::gn_workspace_bytes(n, thw, c, groups);
     if (!workspace || workspace_bytes < need)
         return fail(CONV3D_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
-    conv3d_status st = check_device();
+    st = check_device();
     if (st != CONV3D_OK) return st;
     hipError_t e = c3d::launch_groupnorm_silu(static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(gamma),
                                               static_cast<const _Float16 *>(beta), static_cast<_Float16 *>(y), n, thw,
@@ -577,6 +586,19 @@ conv3d_status conv3d_calibrate_hbm(const void *src, void *dst, size_t bytes, dou
     if (st != CONV3D_OK) return st;
     hipError_t e = c3d::calibrate_hbm(src, dst, bytes, static_cast<hipStream_t>(stream), read_gbs, copy_gbs);
     if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "hbm calibration: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t conv3d_clock_stamp_bytes(void) { return c3d::clock_stamp_bytes(); }
+
+conv3d_status conv3d_clock_stamp(void *out, size_t out_bytes, void *stream) {
+    if (!out || misaligned(out)) return fail(CONV3D_ERR_INVALID_ARG, "out must be a 16-byte aligned device pointer");
+    if (out_bytes < c3d::clock_stamp_bytes())
+        return fail(CONV3D_ERR_WORKSPACE, "out of %zu bytes needed, %zu given", c3d::clock_stamp_bytes(), out_bytes);
+    conv3d_status st = check_device();
+    if (st != CONV3D_OK) return st;
+    hipError_t e = c3d::clock_stamp(out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "clock stamp: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -99,6 +99,8 @@ size_t calibrate_scratch_bytes();
 hipError_t calibrate_mfma(void *scratch, hipStream_t s, double *tflops, double *sclk_mhz);
 hipError_t calibrate_hbm(const void *src, void *dst, size_t bytes, hipStream_t s, double *read_gbs,
                          double *copy_gbs);
+size_t clock_stamp_bytes();
+hipError_t clock_stamp(void *out, hipStream_t s);
 
 // Set the calling thread's conv3d_last_error() message (printf format).
 void set_last_error(const char *fmt, ...);

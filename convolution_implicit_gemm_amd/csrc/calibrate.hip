@@ -11,6 +11,10 @@
 //    reference counter (s_memrealtime).
 //  * HBM: a read-only stream and a copy (read + write), 16-byte non-temporal
 //    accesses, many loads in flight per thread.
+//  * Clock stamps: a tiny kernel whose workgroups record the shader-clock
+//    counter, the 100 MHz reference counter and the id of the XCD they run
+//    on.  Two stamps enqueued around other work give the mean shader clock
+//    of each XCD over that work, without touching the work's own kernels.
 #include <hip/hip_runtime.h>
 
 #include "conv3d.h"
@@ -29,6 +33,7 @@ constexpr int kCalBlocks = 512, kCalThreads = 256;
 constexpr size_t kCalPatternBytes = (size_t)kCalFrags * 64 * 16;
 constexpr size_t kCalClockBytes = (size_t)kCalBlocks * 2 * sizeof(uint64_t);
 constexpr size_t kCalScratch = kCalPatternBytes + kCalClockBytes + 256;
+constexpr int kStampBlocks = 64;
 
 __global__ __launch_bounds__(256) void cal_fill_kernel(uint32_t *p, int64_t words) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -145,7 +150,28 @@ hipError_t time_launches(F launch, int reps, hipStream_t s, float *ms) {
     return e;
 }
 
+// One wave per workgroup; workgroups are dealt to the XCDs round-robin, so
+// kStampBlocks / 8 of them land on each.
+__global__ __launch_bounds__(64) void cal_stamp_kernel(uint64_t *out) {
+    if (threadIdx.x == 0) {
+        uint32_t xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        const uint64_t c = __builtin_amdgcn_s_memtime();
+        const uint64_t r = __builtin_amdgcn_s_memrealtime();
+        out[3 * blockIdx.x] = c;
+        out[3 * blockIdx.x + 1] = r;
+        out[3 * blockIdx.x + 2] = xcc & 0xFu;
+    }
+}
+
 }  // namespace
+
+size_t clock_stamp_bytes() { return (size_t)kStampBlocks * 3 * sizeof(uint64_t); }
+
+hipError_t clock_stamp(void *out, hipStream_t s) {
+    hipLaunchKernelGGL(cal_stamp_kernel, dim3(kStampBlocks), dim3(64), 0, s, static_cast<uint64_t *>(out));
+    return hipGetLastError();
+}
 
 size_t calibrate_scratch_bytes() { return kCalScratch; }
 

@@ -232,6 +232,23 @@ conv3d_status conv3d_calibrate_hbm(const void *src, void *dst, size_t bytes, dou
                                    void *stream);
 
 /*
+ * Measurement aid, not on the convolution path: the mean shader clock over
+ * work enqueued between two stamps.  conv3d_clock_stamp enqueues on `stream`
+ * a tiny kernel (64 one-wave workgroups, dealt round-robin to the 8 XCDs);
+ * workgroup b writes three uint64 at out[3b..3b+2]: the shader-clock counter
+ * (s_memtime, which runs at the shader clock), the 100 MHz reference counter
+ * (s_memrealtime) and the id of the XCD it ran on.  For each XCD, the change
+ * of its mean shader-clock counter between two stamps over the change of its
+ * mean reference counter, times 100 MHz, is that XCD's mean clock over the
+ * work between them.  It neither waits nor synchronises: read `out` after the
+ * stream has passed it.  out: device memory of at least
+ * conv3d_clock_stamp_bytes(), 16-byte aligned, overwritten.
+ * Errors: INVALID_ARG (null or misaligned out), WORKSPACE (too small), HIP.
+ */
+size_t conv3d_clock_stamp_bytes(void);
+conv3d_status conv3d_clock_stamp(void *out, size_t out_bytes, void *stream);
+
+/*
  * Start-up self-test of this library on the current device: tiny
  * integer-valued cases (causal conv with bias and residual, zero-padded conv,
  * the streaming 1x1x1 kernel, the T=1 fold, a plan that splits K, and

@@ -11,8 +11,12 @@ The acceptance bounds (stated once here, used by every GPU test):
                    the smallest fp16 normal, covers SiLU's zero crossing).
 bf16 outputs (8 significant bits): the same with the bf16 ulp in place of the
 fp16 one (conv), or added (GroupNorm, whose relative term is below half a bf16
-ulp); the T=1 fold of bf16 weights adds 2^-9 * S (its one rounding), so the fold
-path of bf16 uses 3e-3 * S.
+ulp).  The T=1 fold of bf16 weights rounds each summed weight once to bf16:
+with 8 significant bits, round-to-nearest-even errs by at most 2^-8 of the
+value, so each folded weight carries at most 2^-8 * sum_tau |w_tau| and the
+output at most 2^-8 * S more; the fold path of bf16 therefore uses
+(2e-3 + 2^-8) * S (BF16_FOLD_REL).  The fp16 fold's one rounding (11
+significant bits, 2^-11 * S <= 4.9e-4 * S) stays inside 2e-3 * S.
 """
 from __future__ import annotations
 
@@ -24,6 +28,7 @@ import torch
 
 import convolution_implicit_gemm_amd as c3d
 
+BF16_FOLD_REL = 2e-3 + 2.0 ** -8  # the bf16 T=1 fold path's relative bound (see above)
 GUARD = 64  # fp16 elements of guard band on each side of every output
 GUARD_BITS = 0x7E5A  # a NaN pattern no kernel writes
 
@@ -221,3 +226,40 @@ def edge_voxels(odims):
                 for ww in sorted({0, w // 2, w - 1}):
                     out.append(((nn * t + tt) * h + hh) * w + ww)
     return out
+
+
+def frame_voxels(odims, frames):
+    """Flat output-voxel indices of every voxel of the given output frames (all samples)."""
+    n, t, h, w, _ = odims
+    hw = h * w
+    out = [np.arange((nn * t + f) * hw, (nn * t + f + 1) * hw, dtype=np.int64)
+           for nn in range(n) for f in sorted(set(int(f) % t for f in frames))]
+    return np.concatenate(out)
+
+
+def row_sample(odims, frac, seed):
+    """A seeded fraction of all output voxels (at least one), sorted."""
+    n, t, h, w, _ = odims
+    total = n * t * h * w
+    k = max(1, int(round(frac * total)))
+    return np.sort(np.random.default_rng(seed).choice(total, k, replace=False)).astype(np.int64)
+
+
+def check_voxels(shape, x, w, b, y_dev, vox, res=None, what="", rel=2e-3, ulp=None):
+    """Every output channel at the voxels `vox`, GPU against the fp64 oracle.
+
+    x, w, b, res are host arrays (x ideally float64: the oracle then reads it
+    without decoding fp16 per product); y_dev is the GPU output (device tensor),
+    gathered at `vox` on the device so that only the checked rows come back.
+    Returns the worst err / bound.
+    """
+    import oracle
+    cout = shape.cout
+    vt = torch.from_numpy(np.ascontiguousarray(vox)).to(y_dev.device)
+    got = y_dev.reshape(-1, cout).index_select(0, vt)
+    got = (host_bits(got) if got.dtype == torch.bfloat16 else got.cpu().numpy())
+    m = np.repeat(vox, cout)
+    co = np.tile(np.arange(cout, dtype=np.int64), vox.size)
+    ref, mag = oracle.conv3d_points(x, w, b, res, shape.pads, shape.tmode, m, co)
+    return assert_conv_close(got.reshape(-1), ref, mag, "%s (%d voxels x %d channels)" % (what, vox.size, cout),
+                             rel=rel, ulp=ulp)

@@ -211,6 +211,26 @@ def test_groupnorm_argument_checks():
     assert gn(wsb=8) == c3d.CONV3D_ERR_WORKSPACE
 
 
+def test_clock_stamp_argument_checks():
+    lib = c3d.load_library()
+    need = c3d.conv3d_clock_stamp_bytes()
+    assert need == 64 * 3 * 8
+    assert lib.conv3d_clock_stamp(None, need, None) == c3d.CONV3D_ERR_INVALID_ARG
+    assert lib.conv3d_clock_stamp(A + 4, need, None) == c3d.CONV3D_ERR_INVALID_ARG
+    assert lib.conv3d_clock_stamp(A, need - 8, None) == c3d.CONV3D_ERR_WORKSPACE
+
+
+def test_sclk_between_pairs_stamps_by_xcd():
+    import numpy as np
+    # two XCDs, 4 stamps each; XCD 0 ran 1.5e6 shader cycles in 1e5 reference ticks (1500 MHz)
+    before = np.array([[1000 + i, 50, i % 2] for i in range(8)], dtype=np.uint64)
+    after = before.copy()
+    after[:, 0] += np.where(after[:, 2] == 0, 1_500_000, 2_000_000).astype(np.uint64)
+    after[:, 1] += 100_000
+    got = c3d.sclk_between(before.reshape(-1), after.reshape(-1))
+    assert got == {0: 1500.0, 1: 2000.0}
+
+
 def test_calibration_argument_checks():
     import ctypes
     lib = c3d.load_library()
@@ -336,3 +356,18 @@ def test_weight_from_ncdhw_matches_torch_conv3d_layout():
     got, _ = oracle.conv3d(x.permute(0, 2, 3, 4, 1).numpy(), w_ours.numpy(), pads=(1, 1, 1, 1),
                            tmode=oracle.TPAD_ZERO)
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_binding_rejects_views_and_host_tensors_before_the_call():
+    import torch
+    p = c3d.conv3d_plan(desc(n=2, t=4, h=8, w=8, c_in=16, c_out=16))
+    x = torch.zeros(2, 6, 8, 8, 16, dtype=torch.float16)
+    view = x[:, 1:5]                      # N = 2: a strided view, not contiguous
+    assert not view.is_contiguous()
+    with pytest.raises(c3d.Conv3dError, match="x is not contiguous"):
+        c3d.conv3d_forward(p, view, A, A + MB, None, A + 2 * MB)
+    with pytest.raises(c3d.Conv3dError, match="on cpu, not on a GPU"):
+        c3d.conv3d_forward(p, x[:, :4].contiguous(), A, A + MB, None, A + 2 * MB)
+    g = torch.zeros(16, dtype=torch.float16)
+    with pytest.raises(c3d.Conv3dError, match="gamma is on cpu"):
+        c3d.groupnorm_silu(A, g, A + MB, A + 2 * MB, 1, 64, 16, 2, 1e-6, True, A + 4 * MB, 1 << 20)

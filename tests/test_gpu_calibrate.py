@@ -22,3 +22,21 @@ def test_hbm_calibration_reports_plausible_bandwidth():
     rd, cp = c3d.conv3d_calibrate_hbm(src, dst, nb)
     assert 1000.0 < rd < 12000.0 and 1000.0 < cp < 12000.0
     assert torch.equal(dst[:4096], src[:4096]) and torch.equal(dst[-4096:], src[-4096:])
+
+
+def test_clock_stamps_cover_every_xcd_and_give_a_plausible_clock():
+    import numpy as np
+    nb = c3d.conv3d_clock_stamp_bytes()
+    before = torch.zeros(nb, dtype=torch.uint8, device="cuda:0")
+    after = torch.zeros_like(before)
+    scratch = torch.empty(c3d.conv3d_calibrate_scratch_bytes(), dtype=torch.uint8, device="cuda:0")
+    c3d.conv3d_clock_stamp(before)
+    c3d.conv3d_calibrate_mfma(scratch)   # a few ms of MFMA load between the stamps (synchronises)
+    c3d.conv3d_clock_stamp(after)
+    torch.cuda.synchronize()
+    b = before.cpu().numpy().view(np.uint64).reshape(-1, 3)
+    a = after.cpu().numpy().view(np.uint64).reshape(-1, 3)
+    assert sorted(set(b[:, 2].tolist())) == list(range(8)) == sorted(set(a[:, 2].tolist()))
+    mhz = c3d.sclk_between(b.reshape(-1), a.reshape(-1))
+    assert sorted(mhz) == list(range(8))
+    assert all(500.0 < v < 2600.0 for v in mhz.values()), mhz

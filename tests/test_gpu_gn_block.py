@@ -15,8 +15,8 @@ import oracle
 import workloads
 from workloads import ConvShape
 
-from helpers import (assert_conv_close, assert_gn_close, check_guards, dev, edge_voxels,
-                     guarded_empty, out_dims, sample_points, conv_desc, workspace_for)
+from helpers import (assert_conv_close, assert_gn_close, check_guards, check_voxels, dev, edge_voxels,
+                     frame_voxels, guarded_empty, out_dims, sample_points, conv_desc, workspace_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -135,6 +135,12 @@ def test_decoder_block_per_stage_full_size():
     assert_gn_close(a2, oracle.groupnorm_silu(c1, d["gamma2"], d["beta2"], 32), "GN2")
     ref, mag = oracle.conv3d_points(a2, d["w2"], d["b2"], d["x"], s.pads, s.tmode, m, co)
     assert_conv_close(out.reshape(-1, s.cout)[m, co], ref, mag, "conv2 + residual")
+    # both convs at every channel of output frames 0, 1 and T-1 (each on the GPU's own input)
+    vox = frame_voxels(od, [0, 1, od[1] - 1])
+    check_voxels(s, a1.astype(np.float64), d["w1"], d["b1"], torch.from_numpy(c1).to("cuda:0"), vox,
+                 what="conv1, frames 0, 1, T-1")
+    check_voxels(s, a2.astype(np.float64), d["w2"], d["b2"], torch.from_numpy(out).to("cuda:0"), vox,
+                 res=d["x"], what="conv2 + residual, frames 0, 1, T-1")
 
 
 def test_decoder_block_end_to_end_small():

@@ -44,3 +44,22 @@ def test_entry_module_exposes_build_and_smoke():
     sys.path.insert(0, ROOT)
     import __graft_entry__ as g
     assert callable(g.build) and callable(g.smoke)
+
+
+def test_bench_parity_gate_passes_the_oracle_and_fails_a_planted_error():
+    # the gate's host logic on a small causal conv: an output equal to the oracle's, rounded
+    # to fp16, passes; the same output with one wrong element (planted on the CPU) fails
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+    import oracle
+    s = workloads.ConvShape(1, 3, 8, 8, 16, 16)
+    d = workloads.conv_inputs(s, 4242)
+    x64, w64, b64 = (d[k].astype(np.float64) for k in ("x", "w", "b"))
+    ref, _ = oracle.conv3d(x64, w64, b64, None, s.pads, s.tmode)
+    y = torch.from_numpy(ref.astype(np.float16))
+    gate = bench.parity_gate(s, x64, w64, b64, y, torch, np)
+    assert gate["passed"] and gate["outputs_checked"] == gate["voxels"] * s.cout
+    bad = y.clone()
+    bad.view(-1, s.cout)[0, 3] += 0.5   # voxel 0 is a corner voxel: always in the gate's sample
+    assert not bench.parity_gate(s, x64, w64, b64, bad, torch, np)["passed"]
