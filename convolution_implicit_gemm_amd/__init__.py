@@ -38,6 +38,7 @@ CONV3D_PATH_POINTWISE = 2
 EXPORTED = ("conv3d_plan", "conv3d_plan_query", "conv3d_plan_destroy", "conv3d_forward",
             "conv3d_forward_chunk",
             "groupnorm_silu_workspace", "groupnorm_silu", "groupnorm_silu_bf16",
+            "groupnorm_silu_noalloc_max_bytes", "groupnorm_silu_noalloc",
             "conv3d_calibrate_scratch_bytes",
             "conv3d_calibrate_mfma", "conv3d_calibrate_hbm", "conv3d_clock_stamp_bytes",
             "conv3d_clock_stamp", "conv3d_status_str",
@@ -101,6 +102,10 @@ def load_library(path: str = LIB_PATH):
     lib.groupnorm_silu_bf16.argtypes = lib.groupnorm_silu.argtypes
     lib.groupnorm_silu_bf16.restype = ctypes.c_int
     lib.groupnorm_silu.restype = ctypes.c_int
+    lib.groupnorm_silu_noalloc_max_bytes.argtypes = []
+    lib.groupnorm_silu_noalloc_max_bytes.restype = sz
+    lib.groupnorm_silu_noalloc.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_float, i32, vp]
+    lib.groupnorm_silu_noalloc.restype = ctypes.c_int
     lib.conv3d_status_str.argtypes = [ctypes.c_int]
     lib.conv3d_status_str.restype = ctypes.c_char_p
     lib.conv3d_last_error.argtypes = []
@@ -273,6 +278,18 @@ def groupnorm_silu(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, worksp
     _check(fn(_addr(x, "x", ne, dt), _addr(gamma, "gamma", c, dt), _addr(beta, "beta", c, dt), _addr(y, "y", ne, dt),
               n, thw, c, groups, float(eps), 1 if apply_silu else 0, _addr(workspace, "workspace"),
               workspace_bytes, _stream(stream)))
+
+
+def groupnorm_silu_noalloc_max_bytes() -> int:
+    return load_library().groupnorm_silu_noalloc_max_bytes()
+
+
+def groupnorm_silu_noalloc(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, stream=None) -> None:
+    """groupnorm_silu (fp16) with the library's static device scratch instead of a workspace."""
+    dt, ne = _elem_dtype(False), n * thw * c
+    _check(load_library().groupnorm_silu_noalloc(_addr(x, "x", ne, dt), _addr(gamma, "gamma", c, dt),
+                                                 _addr(beta, "beta", c, dt), _addr(y, "y", ne, dt), n, thw, c,
+                                                 groups, float(eps), 1 if apply_silu else 0, _stream(stream)))
 
 
 def conv3d_calibrate_scratch_bytes() -> int:

@@ -557,6 +557,31 @@ conv3d_status groupnorm_silu_bf16(const void *x, const void *gamma, const void *
     return gn_entry(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, workspace, workspace_bytes, stream, true);
 }
 
+size_t groupnorm_silu_noalloc_max_bytes(void) { return c3d::kGnStaticScratchBytes; }
+
+conv3d_status groupnorm_silu_noalloc(const void *x, const void *gamma, const void *beta, void *y, int32_t n,
+                                     int64_t thw, int32_t c, int32_t groups, float eps, int32_t apply_silu,
+                                     void *stream) {
+    conv3d_status st = gn_check(x, gamma, beta, y, n, thw, c, groups, eps);
+    if (st != CONV3D_OK) return st;
+    const size_t need = c3d::gn_workspace_bytes(n, thw, c, groups);
+    if (need > c3d::kGnStaticScratchBytes)
+        return fail(CONV3D_ERR_WORKSPACE,
+                    "these sizes need %zu bytes of scratch; the static scratch array of groupnorm_silu_noalloc holds "
+                    "%zu (use groupnorm_silu with a workspace)",
+                    need, c3d::kGnStaticScratchBytes);
+    st = check_device();
+    if (st != CONV3D_OK) return st;
+    void *ws = nullptr;
+    hipError_t e = c3d::gn_static_scratch(&ws);
+    if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "static scratch address: %s", hipGetErrorString(e));
+    e = c3d::launch_groupnorm_silu(static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(gamma),
+                                   static_cast<const _Float16 *>(beta), static_cast<_Float16 *>(y), n, thw, c, groups,
+                                   eps, apply_silu, false, ws, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "groupnorm launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"
 
 size_t conv3d_calibrate_scratch_bytes(void) { return c3d::calibrate_scratch_bytes(); }

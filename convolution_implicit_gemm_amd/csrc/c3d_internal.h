@@ -93,6 +93,10 @@ size_t gn_workspace_bytes(int32_t n, int64_t thw, int32_t c, int32_t groups);
 hipError_t launch_groupnorm_silu(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta,
                                  _Float16 *y, int32_t n, int64_t thw, int32_t c, int32_t groups,
                                  float eps, int32_t silu, bool bf16, void *ws, hipStream_t s);
+// The static device scratch array of groupnorm_silu_noalloc: its size, and
+// its address on the current device (looked up once per device).
+constexpr size_t kGnStaticScratchBytes = (size_t)4 << 20;
+hipError_t gn_static_scratch(void **ptr);
 
 // Measurement aids (calibrate.hip): machine ceilings for the kernels above.
 size_t calibrate_scratch_bytes();

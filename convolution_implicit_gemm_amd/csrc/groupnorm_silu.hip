@@ -24,6 +24,15 @@
 #include "c3d_internal.h"
 #include "elem16.h"
 
+#include <mutex>
+
+// Scratch of groupnorm_silu_noalloc, for callers that cannot allocate device
+// memory: one copy per device, at its own address on each, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: kernels and copies get the address hipGetSymbolAddress
+// returns for the current device (c3d::gn_static_scratch).
+static __device__ __align__(256) unsigned char scratch[c3d::kGnStaticScratchBytes];
+
 namespace c3d {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -315,7 +324,28 @@ hipError_t launch_gn(const _Float16 *x, const _Float16 *gamma, const _Float16 *b
     return hipGetLastError();
 }
 
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices];
+
 }  // namespace
+
+hipError_t gn_static_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(::scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 size_t gn_workspace_bytes(int32_t n, int64_t thw, int32_t c, int32_t groups) {
     const GnGeom g = gn_geom(n, thw, c);

@@ -207,6 +207,27 @@ conv3d_status groupnorm_silu_bf16(const void *x, const void *gamma, const void *
                                   void *stream);
 
 /*
+ * groupnorm_silu for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same operation, arguments, kernels and results as groupnorm_silu on
+ * fp16 data, but no workspace argument.  Its scratch (fp32 partial statistics
+ * and per-channel scale/shift) is a static device array of
+ * groupnorm_silu_noalloc_max_bytes() bytes (4 MiB) in the library, one per
+ * device, held from the first call on a device until the process ends; this
+ * call allocates nothing.  Every call on a device shares that device's array,
+ * so calls that may overlap on one device (other streams, other threads)
+ * race and must not be made; calls in one stream's order are safe.  Nothing
+ * in the array needs to start at zero: each call writes all of it it reads.
+ * Errors: as groupnorm_silu, and WORKSPACE when groupnorm_silu_workspace()
+ * of these sizes exceeds the array (e.g. many groups with a large n); HIP if
+ * the array's device address cannot be found.
+ */
+size_t groupnorm_silu_noalloc_max_bytes(void);
+conv3d_status groupnorm_silu_noalloc(const void *x, const void *gamma, const void *beta, void *y,
+                                     int32_t n, int64_t thw, int32_t c, int32_t groups, float eps,
+                                     int32_t apply_silu, void *stream);
+
+/*
  * Measurement aids, not on the convolution path: the ceilings of the machine
  * the library runs on, to report the kernels' throughput against beside the
  * published peaks.  Both run a few milliseconds of work on `stream`, then

@@ -211,6 +211,33 @@ def test_groupnorm_argument_checks():
     assert gn(wsb=8) == c3d.CONV3D_ERR_WORKSPACE
 
 
+def test_groupnorm_noalloc_argument_checks_and_limit():
+    lib = c3d.load_library()
+    assert c3d.groupnorm_silu_noalloc_max_bytes() == 4 << 20
+
+    def gn(x=A, y=A + 512 * MB, n=1, thw=100, c=256, g=32, eps=1e-6):
+        return lib.groupnorm_silu_noalloc(x, A + 1536 * MB, A + 1600 * MB, y, n, thw, c, g, eps, 1, None)
+    assert gn(x=None) == c3d.CONV3D_ERR_INVALID_ARG
+    assert gn(g=3) == c3d.CONV3D_ERR_INVALID_ARG
+    assert gn(c=96) == c3d.CONV3D_ERR_UNSUPPORTED
+    assert gn(eps=-1.0) == c3d.CONV3D_ERR_INVALID_ARG
+    assert gn(y=A + 1024) == c3d.CONV3D_ERR_INVALID_ARG           # partial overlap
+    # sizes whose scratch exceeds the static array are refused before the device is touched
+    big = (8192, 1024)                                             # c, groups: 8 channels per group
+    assert c3d.groupnorm_silu_workspace(1, 4096, *big) > c3d.groupnorm_silu_noalloc_max_bytes()
+    assert gn(thw=4096, c=big[0], g=big[1]) == c3d.CONV3D_ERR_WORKSPACE
+    assert "static scratch" in c3d.conv3d_last_error()
+    # the decoder-block GroupNorm fits
+    assert c3d.groupnorm_silu_workspace(1, 17 * 128 * 128, 256, 32) <= c3d.groupnorm_silu_noalloc_max_bytes()
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="host without a GPU only")
+def test_groupnorm_noalloc_without_a_device_reports_no_device():
+    lib = c3d.load_library()
+    assert lib.groupnorm_silu_noalloc(A, A + 1536 * MB, A + 1600 * MB, A + 512 * MB, 1, 100, 256, 32, 1e-6, 1,
+                                      None) == c3d.CONV3D_ERR_NO_DEVICE
+
+
 def test_clock_stamp_argument_checks():
     lib = c3d.load_library()
     need = c3d.conv3d_clock_stamp_bytes()
