@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libconv3d.so")
-SOURCES = ["conv3d_igemm.hip", "pointwise.hip", "groupnorm_silu.hip", "calibrate.hip", "api.cpp", "selftest.cpp"]
+SOURCES = ["conv3d_igemm.hip", "conv3d_ps.hip", "pointwise.hip", "groupnorm_silu.hip", "calibrate.hip", "api.cpp", "selftest.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

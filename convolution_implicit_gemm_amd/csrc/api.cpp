@@ -267,6 +267,7 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
     for (int i = 0; i < ntile; ++i) {
         const c3d::TileCfg &t = tiles[i];
         if (forced && *forced && strcmp(forced, t.name) != 0) continue;
+        if (t.supported && !t.supported(q)) continue;
         const int64_t mt = (q.M + t.bm - 1) / t.bm, nt = (q.Cout + t.bn - 1) / t.bn;
         const int cpt = (q.Cin + t.bk - 1) / t.bk;
         const Decomp dcmp = decompose(t, mt * nt, q.kt * q.kh * q.kw * cpt, skmode);

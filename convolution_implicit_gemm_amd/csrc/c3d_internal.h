@@ -55,9 +55,17 @@ struct TileCfg {
     ConvLaunchFn launch_full;  // Cin % bk == 0
     ConvLaunchFn launch_tail;  // any Cin % 8 == 0 (channel tail zero-filled per tap)
     ConvLaunchFn launch_fixup; // sums the K-pieces of the split tiles, then the epilogue
+    bool (*supported)(const ConvParams &q);  // null: every shape; else the shapes it runs
 };
 
 const TileCfg *tile_table(int *count);
+
+// The row-slab ping-pong kernel (conv3d_ps.hip): 256 voxels x 256 channels x
+// 64, for kw = 3 with pw = 1, kt, kh <= 3, and output rows that tile 256-voxel
+// blocks (Wo a multiple of 32 dividing 256, or a multiple of 256).
+bool ps_supported(const ConvParams &q);
+template <bool TAIL>
+hipError_t launch_ps(const ConvParams &p, hipStream_t s);
 
 // 1x1x1 convolution without padding: a streaming GEMM over voxels.
 struct PwParams {

@@ -1,0 +1,398 @@
+// Implicit-GEMM fp16 3D convolution for gfx950: row slabs, ping-pong schedule.
+//
+// The GEMM is that of conv3d_igemm.hip (rows = output voxels, columns = output
+// channels, K = (tau, r, s, ci) gathered on the fly from the NDHWC input: the
+// implicit-GEMM lowering of the Draw Things engineering feed's post on the
+// Codex-written Metal conv3d shaders).  This kernel covers the common video-VAE
+// shape, 3 taps along w with one voxel of zero padding (kw = 3, pw = 1), output
+// rows a multiple of 32 voxels long that tile 256-voxel blocks (Wo | 256 or
+// 256 | Wo), at most 3 taps along t and h.  Tile: 256 voxels x 256 output
+// channels, 64 input channels per K-stage, 8 waves.
+//
+// Row slabs.  A tile's 256 output voxels are R = 256 / L segments of L =
+// min(Wo, 256) voxels, each inside one output row.  For one channel slice and
+// one (tau, r) the three taps s = 0, 1, 2 read, per segment, the same input
+// row shifted by one voxel: input voxels w0 - 1 .. w0 + L.  So the kernel
+// loads that slab (R * (L + 2) voxels x 64 channels, zero where it leaves the
+// frame) into LDS once, and the three K-stages (tau, r, s) read their MFMA
+// B-fragments from it at slab row (segment * (L + 2) + v + s).  Against one
+// activation tile per stage this loads 40 instead of 96 1-KiB instructions per
+// three stages and computes the gather offsets once per slab instead of once
+// per stage.  The slab rows carry their own bank swizzle, chunk ^ ((row >> 1)
+// & 7), which keeps every 16 consecutive rows read at one chunk in distinct
+// banks whatever the shift s.
+//
+// Ping-pong.  The 8 waves form two groups of 4, one wave of each on every SIMD
+// (waves w and w + 4 share a SIMD).  Group g owns output channels 128g ..
+// 128g + 127, loads and reads only its own half of each weight stage, and
+// alternates between a memory phase (the MFMA fragments of two k-steps from
+// LDS into registers, its share of the global->LDS loads) and a compute phase
+// (those 16 MFMAs, at raised wave priority).  The groups run one phase apart
+// with one workgroup barrier per phase, so each SIMD's matrix core is fed by
+// one wave while the other reads LDS and issues loads.
+//
+// Pipeline, per group g, K-stage k (tile-local), phases 4k + g (k-steps 0-1)
+// and 4k + 2 + g (k-steps 2-3):
+//   weights  2 buffers per group; stage k + 1 is fetched in the memory phase
+//            of k-steps 0-1 of stage k (its buffer held stage k - 1, which the
+//            group finished reading one phase before) and waited for at the
+//            end of the group's compute phase of k-steps 2-3 (4 phases of
+//            lead);
+//   slabs    2 buffers; the slab of the next three stages is fetched in the
+//            memory phases of the first one and a half stages of the current
+//            slab (5 instructions per wave) and waited for by the end of its
+//            second stage.
+// K-pieces of a split tile start and end on slab boundaries.
+#include "igemm_common.h"
+
+namespace c3d {
+
+namespace {
+
+constexpr int kPsThreads = 512;
+constexpr int kPsBM = 256, kPsBN = 256, kPsBK = 64;
+constexpr int kPsWM = 64, kPsWN = 128;
+constexpr int kPsTM = kPsWM / 32, kPsTN = kPsWN / 32;
+constexpr int kPsRB = kPsBK * 2;                  // bytes per LDS row
+constexpr int kPsWHalf = 128 * kPsRB;             // one group's half of one weight stage: 16 KiB
+constexpr int kPsSlabRows = 320;                  // 40 load instructions; R * (L + 2) <= 264 rows are used
+constexpr int kPsSlabBytes = kPsSlabRows * kPsRB; // 40 KiB
+constexpr int kPsSlabBase = 4 * kPsWHalf;         // weights: [group][buffer] halves, then the 2 slabs
+constexpr int kPsLds = kPsSlabBase + 2 * kPsSlabBytes;  // 144 KiB
+constexpr int kPsSlabSlots = kPsSlabRows / 8 / 8;       // slab load instructions per wave: 5
+static_assert(kPsLds <= 160 * 1024, "LDS is 160 KiB per CU");
+
+// Bank swizzle of a slab row: any 16 consecutive rows read at one logical
+// chunk occupy 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int slab_swz(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ void ps_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+template <int N>
+__device__ __forceinline__ void ps_wait_loads() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+}  // namespace
+
+template <bool TAIL, typename E>
+__global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[kPsLds];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wv >> 2;            // waves 0-3 and 4-7: one of each per SIMD
+    const int gw = wv & 3;              // wave within the group
+    const int wmi = gw, wni = grp;      // this wave's 64 voxels and 128 output channels
+
+    // Work: whole tiles in XCD-contiguous ranges, then K-pieces of the split
+    // tiles, cut on slab (3-stage) boundaries.
+    const int bid = blockIdx.x;
+    int tile, it0 = 0, it1 = p.niter, slot = -1;
+    if (bid < p.dp_tiles) {
+        const int per = p.dp_tiles >> 3, rem = p.dp_tiles & 7;
+        const int xcd = bid & 7;
+        tile = xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3);
+    } else {
+        slot = bid - p.dp_tiles;
+        const int piece = slot % p.sk_pieces;
+        tile = p.dp_tiles + slot / p.sk_pieces;
+        const int nslab = p.niter / 3;
+        it0 = 3 * (int)((int64_t)nslab * piece / p.sk_pieces);
+        it1 = 3 * (int)((int64_t)nslab * (piece + 1) / p.sk_pieces);
+    }
+    const int mt = tile / p.n_tiles, nt = tile - mt * p.n_tiles;
+    const int m0 = mt * kPsBM;
+    const int n0 = nt * kPsBN;
+
+    const int T = p.T, H = p.H, W = p.W, Cin = p.Cin;
+    const int HW = H * W;
+    const int M = (int)p.M;
+    const int L = p.Wo < kPsBM ? p.Wo : kPsBM;  // voxels per segment
+    const int LS = L + 2;                       // slab rows per segment
+
+    auto vb_of = [&](int m, int &to, int &ho, int &wo) {
+        wo = m % p.Wo;
+        const int r1 = m / p.Wo;
+        ho = r1 % p.Ho;
+        const int r2 = r1 / p.Ho;
+        to = r2 % p.To;
+        const int n = r2 / p.To;
+        return ((n * T + to) * H + ho) * W + wo;
+    };
+
+    // this tile's window of input voxels: [lo, hi)
+    int lo, hi;
+    {
+        int t_, h_, w_;
+        const int m_last = (m0 + kPsBM < M ? m0 + kPsBM : M) - 1;
+        lo = vb_of(m0, t_, h_, w_) - (p.ptf * HW + p.ph * W + p.pw);
+        lo = lo < 0 ? 0 : lo;
+        hi = vb_of(m_last, t_, h_, w_) + (p.kt - 1 - p.ptf) * HW + (p.kh - 1 - p.ph) * W + (p.kw - 1 - p.pw) + 1;
+        hi = hi > p.in_vox ? p.in_vox : hi;
+        if (hi < lo) hi = lo;
+    }
+    const buf_rsrc xr = make_rsrc(p.x + (int64_t)lo * Cin, (uint32_t)(hi - lo) * (uint32_t)Cin * 2u);
+    const buf_rsrc wr = make_rsrc(p.w, p.w_bytes);
+    const int lrow = lane >> 3, lchunk = lane & 7;
+    const int cin2 = Cin * 2;
+
+    // ---- slab slots: instruction q = 8j + wave fills slab rows 8q .. 8q+7.
+    // Per lane, the window byte offset of its slab row's voxel at temporal tap
+    // 0 and row tap 0 (the replicate clamp applied), the steps to taps 1 and 2
+    // in t, and the validity of each (tau, r): bit 8 + r, bit 16 + tau.
+    uint32_t s_tb0[kPsSlabSlots], s_d1[kPsSlabSlots], s_d2[kPsSlabSlots], s_ok[kPsSlabSlots];
+    int s_c8[kPsSlabSlots];
+#pragma unroll
+    for (int j = 0; j < kPsSlabSlots; ++j) {
+        const int row = (j * 8 + wv) * 8 + lrow;
+        const int seg = row / LS, u = row - seg * LS;
+        const int chunk = lchunk ^ slab_swz(row);
+        s_c8[j] = chunk * 8;
+        s_tb0[j] = s_d1[j] = s_d2[j] = s_ok[j] = 0;
+        const int m = m0 + seg * L;             // first voxel of the segment
+        if (seg * L < kPsBM && m < M) {
+            int to, ho, wo;
+            const int vb = vb_of(m, to, ho, wo);
+            const int wi = wo + u - p.pw;       // input column of this slab row
+            if ((unsigned)wi < (unsigned)W) {
+                // rel: the row's voxel at (t = to - ptf, h = ho - ph), before clamping
+                const int base = vb - to * HW - ho * W - wo + wi - lo;  // voxel (n, 0, 0, wi) - lo
+                uint32_t tb[3], ok = 0;
+#pragma unroll
+                for (int tau = 0; tau < 3; ++tau) {
+                    int ts = to + tau - p.ptf;
+                    const bool inside = (unsigned)ts < (unsigned)T;
+                    if (p.replicate) ts = ts < 0 ? 0 : (ts > T - 1 ? T - 1 : ts);
+                    tb[tau] = (uint32_t)(base + ts * HW + (ho - p.ph) * W) * (uint32_t)cin2 + (uint32_t)chunk * 16u;
+                    ok |= (uint32_t)(tau < p.kt && (inside || p.replicate)) << (16 + tau);
+                }
+                for (int r = 0; r < p.kh; ++r) ok |= (uint32_t)((unsigned)(ho + r - p.ph) < (unsigned)H) << (8 + r);
+                s_tb0[j] = tb[0];
+                s_d1[j] = tb[1] - tb[0];
+                s_d2[j] = tb[2] - tb[1];
+                s_ok[j] = ok;
+            }
+        }
+    }
+    // ---- weight slots: instruction q = 4j + gw of group g fills rows 8q .. 8q+7
+    // of the group's half (output channels n0 + 128g + ...)
+    uint32_t b_voff[4];
+    int b_c8[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = (j * 4 + gw) * 8 + lrow;
+        const int co = n0 + grp * 128 + row;
+        b_c8[j] = (lchunk ^ swz<kPsBK>(row)) * 8;
+        b_voff[j] = co < p.Cout ? (uint32_t)(co * p.K + b_c8[j]) * 2u : kOOB;
+    }
+
+    // ---- cursors.  Weights: one stage ahead of the stage computed; slabs: one
+    // slab ahead.  Each freezes on the tile's last stage / slab, so the extra
+    // fetches that keep every wave's load count constant re-read valid data.
+    const int ntaps = p.kt * p.kh * 3;
+    int w_it = it0, w_ci = (it0 / ntaps) * kPsBK, w_tap = it0 % ntaps;
+    int s_it = it0, s_ci = w_ci, s_tr = w_tap / 3;  // slab: (tau, r) index = tap / 3
+    auto advance_w = [&]() {
+        const int step = w_it + 1 < it1 ? 1 : 0;
+        ++w_it;
+        const int nt_ = w_tap + step;
+        const int wrap = nt_ == ntaps ? 1 : 0;
+        w_tap = wrap ? 0 : nt_;
+        w_ci += kPsBK * wrap;
+    };
+    auto advance_s = [&]() {
+        const int step = s_it + 3 < it1 ? 1 : 0;
+        s_it += 3;
+        const int ntr = s_tr + step;
+        const int wrap = ntr == p.kt * p.kh ? 1 : 0;
+        s_tr = wrap ? 0 : ntr;
+        s_ci += kPsBK * wrap;
+    };
+    uint32_t s_voff[kPsSlabSlots];
+    auto set_slab_offsets = [&]() {
+        const int tau = s_tr / p.kh, r = s_tr - tau * p.kh;
+        const uint32_t sel = (1u << (8 + r)) | (1u << (16 + tau));
+        const uint32_t m1 = tau >= 1 ? ~0u : 0u, m2 = tau >= 2 ? ~0u : 0u;
+        const uint32_t rsc = (uint32_t)(r * W) * (uint32_t)cin2;
+#pragma unroll
+        for (int j = 0; j < kPsSlabSlots; ++j) {
+            const uint32_t off = s_tb0[j] + (s_d1[j] & m1) + (s_d2[j] & m2) + rsc;
+            s_voff[j] = (s_ok[j] & sel) == sel ? off : kOOB;
+        }
+    };
+    auto fire_w = [&](int wbuf) {
+        char *sb = smem + (grp * 2 + wbuf) * kPsWHalf;
+        const uint32_t s_w = (uint32_t)(w_tap * Cin + w_ci) * 2u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t v = (!TAIL || w_ci + b_c8[j] < Cin) ? b_voff[j] : kOOB;
+            dma16(wr, sb + (j * 4 + gw) * 1024, v, s_w);
+        }
+    };
+    auto fire_s = [&](int sbuf, int j) {
+        char *sb = smem + kPsSlabBase + sbuf * kPsSlabBytes;
+        const uint32_t v = (!TAIL || s_ci + s_c8[j] < Cin) ? s_voff[j] : kOOB;
+        dma16(xr, sb + (j * 8 + wv) * 1024, v, (uint32_t)s_ci * 2u);
+    };
+
+    // ---- fragment offsets.  Weights (MFMA A): rows 32i + lane%32 of the
+    // group's half.  Slab (MFMA B), fragment j at shift s: slab row
+    // seg * LS + v + lane%32 + s for the fragment's segment seg and start v.
+    const int rrow = lane & 31, rhi = lane >> 5;
+    int koff_w[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) koff_w[kk] = rrow * kPsRB + (((2 * kk + rhi) ^ swz<kPsBK>(rrow)) * 16);
+    int koff_b[kPsTM][3][4];
+#pragma unroll
+    for (int j = 0; j < kPsTM; ++j) {
+        const int v = wmi * kPsWM + j * 32;
+        const int seg = v / L, v0 = v - seg * L;
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            const int row = seg * LS + v0 + rrow + s;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                koff_b[j][s][kk] = kPsSlabBase + row * kPsRB + (((2 * kk + rhi) ^ slab_swz(row)) * 16);
+        }
+    }
+
+    f32x16 acc[kPsTN][kPsTM];
+#pragma unroll
+    for (int i = 0; i < kPsTN; ++i)
+#pragma unroll
+        for (int j = 0; j < kPsTM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    half8_t af[2][kPsTN], bf[2][kPsTM];
+    // fragments of k-steps KK0, KK0 + 1 at slab shift S
+    auto read_half = [&](int wbuf, int sbuf, auto kk0c, auto sc) {
+        constexpr int KK0 = decltype(kk0c)::value, S = decltype(sc)::value;
+        const char *wsb = smem + (grp * 2 + wbuf) * kPsWHalf;
+        const char *ssb = smem + sbuf * kPsSlabBytes;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < kPsTN; ++i)
+                af[h][i] = *reinterpret_cast<const half8_t *>(wsb + i * 32 * kPsRB + koff_w[KK0 + h]);
+#pragma unroll
+            for (int j = 0; j < kPsTM; ++j)
+                bf[h][j] = *reinterpret_cast<const half8_t *>(ssb + koff_b[j][S][KK0 + h]);
+        }
+    };
+    auto mfma_half = [&]() {
+        __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < kPsTN; ++i)
+#pragma unroll
+                for (int j = 0; j < kPsTM; ++j) acc[i][j] = mfma_32x32x16<E>(af[h][i], bf[h][j], acc[i][j]);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // ---- prologue: this group's weights of the first stage and the first slab
+    fire_w(0);
+    advance_w();
+    set_slab_offsets();
+#pragma unroll
+    for (int j = 0; j < kPsSlabSlots; ++j) fire_s(0, j);
+    advance_s();
+    set_slab_offsets();
+    ps_wait_loads<0>();
+    ps_barrier();
+    if (grp) ps_barrier();  // group 1 runs one phase behind
+
+    int wb = 0, sbf = 0;  // buffers of the stage / slab computed
+    for (int it = it0; it < it1; it += 3) {
+        const bool last = it + 3 >= it1;
+        // Three stages of one slab (shift s = 0, 1, 2).  Per wave: slab loads
+        // 0, 1 with the first stage's first memory phase, 2, 3 with its second,
+        // 4 with the second stage's first; weights of the next stage in every
+        // stage's first memory phase.
+        static_for<3>([&](auto sc) {
+            constexpr int S = decltype(sc)::value;
+            read_half(wb, sbf, std::integral_constant<int, 0>{}, sc);
+            if constexpr (S == 0) {
+                fire_s(sbf ^ 1, 0);
+                fire_s(sbf ^ 1, 1);
+            } else if constexpr (S == 1) {
+                fire_s(sbf ^ 1, 4);
+                advance_s();
+                set_slab_offsets();
+            }
+            fire_w(wb ^ 1);
+            advance_w();
+            ps_barrier();
+            mfma_half();
+            ps_barrier();
+            read_half(wb, sbf, std::integral_constant<int, 2>{}, sc);
+            if constexpr (S == 0) {
+                fire_s(sbf ^ 1, 2);
+                fire_s(sbf ^ 1, 3);
+            }
+            ps_barrier();
+            mfma_half();
+            // this group's weights of the next stage (and, after the second
+            // stage, every slab load) have landed before the group's next
+            // memory phase
+            if constexpr (S == 0)
+                ps_wait_loads<2>();
+            else
+                ps_wait_loads<0>();
+            // group 1's very last barrier would pair with nothing
+            if (!(grp && last && S == 2)) ps_barrier();
+            wb ^= 1;
+        });
+        sbf ^= 1;
+    }
+    ps_wait_loads<0>();
+
+    if (slot >= 0) {
+        // a K-piece: the fp32 partial in fragment order, indexed as the fixup
+        // kernel of the 8-wave 256x256 tile expects (wave = wmi * 2 + wni)
+        const int vw = wmi * 2 + wni;
+        f32x4 *pp = reinterpret_cast<f32x4 *>(p.partial + (size_t)slot * (kPsBM * kPsBN));
+#pragma unroll
+        for (int i = 0; i < kPsTN; ++i)
+#pragma unroll
+            for (int j = 0; j < kPsTM; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+                    pp[((((size_t)vw * kPsTN + i) * kPsTM + j) * 4 + g) * 64 + lane] = v;
+                }
+        return;
+    }
+    store_tile<E, kPsTN, kPsTM, kPsWN, kPsWM>(p, acc, m0, kPsBM, n0, wmi, wni, rrow, rhi);
+}
+
+bool ps_supported(const ConvParams &q) {
+    const int L = q.Wo < kPsBM ? q.Wo : kPsBM;
+    const int R = kPsBM / L;
+    return q.kw == 3 && q.pw == 1 && q.kt <= 3 && q.kh <= 3 && q.Wo % 32 == 0 &&
+           (q.Wo % kPsBM == 0 || kPsBM % q.Wo == 0) && R * (L + 2) <= kPsSlabRows;
+}
+
+template <bool TAIL>
+hipError_t launch_ps(const ConvParams &p, hipStream_t s) {
+    const unsigned grid = (unsigned)(p.dp_tiles + p.sk_tiles * p.sk_pieces);
+    if (p.bf16)
+        hipLaunchKernelGGL((conv3d_ps_kernel<TAIL, __bf16>), dim3(grid), dim3(kPsThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((conv3d_ps_kernel<TAIL, _Float16>), dim3(grid), dim3(kPsThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template hipError_t launch_ps<false>(const ConvParams &p, hipStream_t s);
+template hipError_t launch_ps<true>(const ConvParams &p, hipStream_t s);
+
+}  // namespace c3d

@@ -16,7 +16,7 @@ def test_conv_binding_checks_dtype_and_size_before_the_call():
     y = torch.empty(1, 4, 8, 8, 16, dtype=torch.float16, device="cuda:0")
     with pytest.raises(c3d.Conv3dError, match="x is torch.bfloat16"):
         c3d.conv3d_forward(p, x.view(torch.bfloat16), w, b, None, y)
-    with pytest.raises(c3d.Conv3dError, match="y holds 4096 elements"):
+    with pytest.raises(c3d.Conv3dError, match="y holds 1024 elements, 4096 needed"):
         c3d.conv3d_forward(p, x, w, b, None, y[:, :1].contiguous())
     with pytest.raises(c3d.Conv3dError, match="weight holds"):
         c3d.conv3d_forward(p, x, w[:8], b, None, y)

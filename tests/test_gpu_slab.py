@@ -1,0 +1,113 @@
+"""GPU parity of the row-slab kernel (m256n256k64ps) against the fp64 oracle.
+
+The kernel covers kw = 3 with pw = 1, kt, kh <= 3 and output rows that tile
+256-voxel blocks (Wo a multiple of 32 dividing 256, or a multiple of 256).
+Ternary inputs make every partial sum a small integer, so outputs must match
+the oracle bit for bit: every row length it takes, both temporal modes, a
+channel tail, two samples, an M tail (a last tile past the output), the K
+split, bias + residual, bf16, and the first-frame fold (kt = 1 after folding).
+"""
+import numpy as np
+import pytest
+import torch
+
+import convolution_implicit_gemm_amd as c3d
+import oracle
+import workloads
+from workloads import ConvShape, TPAD_REPLICATE as R, TPAD_ZERO as Z
+
+from helpers import assert_conv_close, dev, host_bits, out_dims, run_conv
+
+pytestmark = pytest.mark.gpu
+TILE = "m256n256k64ps"
+
+
+def ternary(shape, seed):
+    return np.random.default_rng(seed).integers(-1, 2, size=shape).astype(np.float16)
+
+
+def oracle_full(s, x, w, b=None, res=None):
+    f = lambda a: None if a is None else np.asarray(a, dtype=np.float64)
+    return oracle.conv3d(f(x), f(w), f(b), f(res), s.pads, s.tmode)
+
+
+SLAB_CASES = [
+    ConvShape(1, 3, 4, 256, 64, 64),                                       # one segment per tile
+    ConvShape(1, 3, 6, 128, 64, 96),                                       # two segments, Cout < 256
+    ConvShape(2, 3, 8, 64, 72, 64),                                        # four segments, N = 2, channel tail
+    ConvShape(1, 2, 8, 32, 40, 264),                                       # eight segments, tail, two column tiles
+    ConvShape(1, 3, 4, 512, 16, 32, pad_t_front=1, pad_t_back=1, tmode=Z),  # 256 | W, symmetric zero
+    ConvShape(1, 3, 3, 32, 64, 64, pad_t_front=2, tmode=Z),                # M = 288: a partial last tile
+    ConvShape(1, 4, 5, 64, 128, 128, kt=1, kh=3, pad_t_front=0),           # kt = 1 (a 2D conv per frame)
+    ConvShape(1, 3, 5, 64, 64, 64, kt=2, kh=2, pad_t_front=1, pad_h=1),    # even extents in t and h
+]
+
+
+@pytest.mark.parametrize("case", range(len(SLAB_CASES)))
+def test_slab_kernel_ternary_bit_exact(case):
+    s = SLAB_CASES[case]
+    x = ternary(s.x_shape, 300 + case)
+    w = ternary(s.w_shape, 320 + case)
+    b = np.random.default_rng(340 + case).integers(-2, 3, s.cout).astype(np.float16)
+    y, info = run_conv(s, x, w, b, tile=TILE)
+    assert info.kernel_name.decode().startswith("conv3d_igemm_" + TILE)
+    ref, _ = oracle_full(s, x, w, b)
+    assert np.array_equal(y.astype(np.float64), ref), "%d of %d outputs differ" % (
+        int((y.astype(np.float64) != ref).sum()), y.size)
+
+
+def test_slab_kernel_k_split_exact_and_equal_to_whole_tiles():
+    s = ConvShape(1, 3, 8, 128, 64, 96)
+    x, w = ternary(s.x_shape, 360), ternary(s.w_shape, 361)
+    b = np.random.default_rng(362).integers(-2, 3, s.cout).astype(np.float16)
+    y1, i1 = run_conv(s, x, w, b, tile=TILE, split="1")
+    assert i1.split_tiles > 0 and i1.split_pieces >= 2
+    y0, i0 = run_conv(s, x, w, b, tile=TILE, split="0")
+    assert i0.split_tiles == 0
+    ref, _ = oracle_full(s, x, w, b)
+    assert np.array_equal(y1.astype(np.float64), ref)
+    assert np.array_equal(y0, y1)
+
+
+def test_slab_kernel_random_with_bias_and_residual_within_bound():
+    s = ConvShape(1, 5, 16, 128, 256, 256)
+    d = workloads.conv_inputs(s, 370)
+    res = workloads.normal_f16(np.random.SeedSequence(371), out_dims(s))
+    y, info = run_conv(s, d["x"], d["w"], d["b"], res=res, tile=TILE)
+    ref, mag = oracle_full(s, d["x"], d["w"], d["b"], res)
+    assert_conv_close(y, ref, mag, "slab kernel + residual")
+    # the same through a K split: the partials' fixup adds bias and residual
+    y2, i2 = run_conv(s, d["x"], d["w"], d["b"], res=res, tile=TILE, split="1")
+    assert i2.split_tiles > 0
+    assert_conv_close(y2, ref, mag, "slab kernel + residual, K split")
+
+
+def test_slab_kernel_bf16_ternary_exact():
+    s = ConvShape(1, 3, 6, 64, 64, 128)
+    x = workloads.ternary_f16(np.random.SeedSequence(380), s.x_shape)
+    w = workloads.ternary_f16(np.random.SeedSequence(381), s.w_shape)
+    to_bf = lambda a: (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y, info = run_conv(s, to_bf(x), to_bf(w), tile=TILE)
+    ref, _ = oracle_full(s, x, w)
+    got = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("tmode", [R, Z])
+def test_slab_kernel_first_frame_fold_exact(tmode):
+    # T = 1: the fold sums the temporal taps and runs a kt = 1 conv, here on the slab kernel
+    s = ConvShape(1, 1, 8, 128, 64, 64, tmode=tmode)
+    x, w = ternary(s.x_shape, 390 + tmode), ternary(s.w_shape, 392 + tmode)
+    y, info = run_conv(s, x, w, tile=TILE)
+    assert info.path == c3d.CONV3D_PATH_T1_FOLD
+    ref, _ = oracle_full(s, x, w)
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+def test_slab_kernel_rejects_shapes_it_does_not_cover():
+    # rows of 48 voxels neither divide nor are a multiple of 256: forcing the tile plans nothing
+    import os
+    from helpers import conv_desc, forced_tile
+    with forced_tile(TILE):
+        with pytest.raises(c3d.Conv3dError):
+            c3d.conv3d_plan(conv_desc(ConvShape(1, 3, 4, 48, 64, 64)))
