@@ -33,15 +33,13 @@
 //
 // Pipeline, per group g, K-stage k (tile-local), phases 4k + g (k-steps 0-1)
 // and 4k + 2 + g (k-steps 2-3):
-//   weights  2 buffers per group; stage k + 1 is fetched in the memory phase
-//            of k-steps 0-1 of stage k (its buffer held stage k - 1, which the
-//            group finished reading one phase before) and waited for at the
-//            end of the group's compute phase of k-steps 2-3 (4 phases of
-//            lead);
-//   slabs    2 buffers; the slab of the next three stages is fetched in the
-//            memory phases of the first one and a half stages of the current
-//            slab (5 instructions per wave) and waited for by the end of its
-//            second stage.
+//   weights  2 buffers per group; stage k + 1 is fetched half in each memory
+//            phase of stage k (its buffer held stage k - 1, which the group
+//            finished reading one phase before) and waited for at the end of
+//            the group's compute phase of k-steps 2-3;
+//   slabs    2 buffers; the slab of the next three stages is fetched one
+//            instruction per memory phase (5 per wave) during the current
+//            slab and waited for before the barrier that starts the next.
 // K-pieces of a split tile start and end on slab boundaries.
 #include "igemm_common.h"
 
@@ -226,11 +224,13 @@ __global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
             s_voff[j] = (s_ok[j] & sel) == sel ? off : kOOB;
         }
     };
-    auto fire_w = [&](int wbuf) {
+    // this wave's weight loads J0, J0 + 1 of the stage at the weight cursor
+    auto fire_w = [&](int wbuf, auto j0c) {
+        constexpr int J0 = decltype(j0c)::value;
         char *sb = smem + (grp * 2 + wbuf) * kPsWHalf;
         const uint32_t s_w = (uint32_t)(w_tap * Cin + w_ci) * 2u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = J0; j < J0 + 2; ++j) {
             const uint32_t v = (!TAIL || w_ci + b_c8[j] < Cin) ? b_voff[j] : kOOB;
             dma16(wr, sb + (j * 4 + gw) * 1024, v, s_w);
         }
@@ -298,7 +298,8 @@ __global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
     };
 
     // ---- prologue: this group's weights of the first stage and the first slab
-    fire_w(0);
+    fire_w(0, std::integral_constant<int, 0>{});
+    fire_w(0, std::integral_constant<int, 2>{});
     advance_w();
     set_slab_offsets();
 #pragma unroll
@@ -312,38 +313,39 @@ __global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
     int wb = 0, sbf = 0;  // buffers of the stage / slab computed
     for (int it = it0; it < it1; it += 3) {
         const bool last = it + 3 >= it1;
-        // Three stages of one slab (shift s = 0, 1, 2).  Per wave: slab loads
-        // 0, 1 with the first stage's first memory phase, 2, 3 with its second,
-        // 4 with the second stage's first; weights of the next stage in every
-        // stage's first memory phase.
+        // Three stages of one slab (shift s = 0, 1, 2).  Every memory phase
+        // issues two of the wave's four weight loads of the next stage and one
+        // of its five loads of the next slab (none in the very last): spread
+        // evenly, the loads never queue up behind one another long enough to
+        // hold a memory phase past its compute phase.
         static_for<3>([&](auto sc) {
             constexpr int S = decltype(sc)::value;
             read_half(wb, sbf, std::integral_constant<int, 0>{}, sc);
-            if constexpr (S == 0) {
-                fire_s(sbf ^ 1, 0);
-                fire_s(sbf ^ 1, 1);
-            } else if constexpr (S == 1) {
-                fire_s(sbf ^ 1, 4);
-                advance_s();
-                set_slab_offsets();
-            }
-            fire_w(wb ^ 1);
-            advance_w();
+            fire_w(wb ^ 1, std::integral_constant<int, 0>{});
+            fire_s(sbf ^ 1, 2 * S);
             ps_barrier();
             mfma_half();
             ps_barrier();
             read_half(wb, sbf, std::integral_constant<int, 2>{}, sc);
-            if constexpr (S == 0) {
-                fire_s(sbf ^ 1, 2);
-                fire_s(sbf ^ 1, 3);
+            fire_w(wb ^ 1, std::integral_constant<int, 2>{});
+            advance_w();
+            if constexpr (S < 2) {
+                fire_s(sbf ^ 1, 2 * S + 1);
+            } else {
+                advance_s();
+                set_slab_offsets();
+                // group 1 ends phase 4k + 3 here: its slab loads (all but the
+                // two weight loads just issued) land before group 0 reads the
+                // next slab
+                if (grp) ps_wait_loads<2>();
             }
             ps_barrier();
             mfma_half();
-            // this group's weights of the next stage (and, after the second
-            // stage, every slab load) have landed before the group's next
-            // memory phase
-            if constexpr (S == 0)
-                ps_wait_loads<2>();
+            // the group's weights of the next stage have landed before its
+            // next memory phase (a slab load issued after them may fly on,
+            // except in the slab's last stage)
+            if constexpr (S < 2)
+                ps_wait_loads<1>();
             else
                 ps_wait_loads<0>();
             // group 1's very last barrier would pair with nothing
