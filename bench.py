@@ -49,7 +49,7 @@ def log(msg):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("conv3d_igemm.hip", "c3d_internal.h"):
+    for f in ("conv3d_igemm.hip", "conv3d_ps.hip", "igemm_common.h", "c3d_internal.h"):
         with open(os.path.join(ROOT, "convolution_implicit_gemm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
