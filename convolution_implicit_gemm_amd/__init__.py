@@ -327,18 +327,20 @@ def conv3d_clock_stamp(out, out_bytes=None, stream=None) -> None:
 
 def sclk_between(before, after):
     """Mean shader clock (MHz) per XCD between two stamps (host uint64 arrays
-    of conv3d_clock_stamp's layout): {xcd: MHz}."""
+    of conv3d_clock_stamp's layout): {xcd: MHz}.  Stamps are paired by the CU
+    they ran on, since the counters of different CUs are not aligned; an XCD's
+    figure is the median over its CUs stamped both times."""
     import numpy as np
     b = np.asarray(before, dtype=np.uint64).reshape(-1, 3)
     a = np.asarray(after, dtype=np.uint64).reshape(-1, 3)
-    out = {}
-    for x in sorted(set(b[:, 2].tolist()) & set(a[:, 2].tolist())):
-        bb, aa = b[b[:, 2] == x], a[a[:, 2] == x]
+    per_xcd = {}
+    for loc in sorted(set(b[:, 2].tolist()) & set(a[:, 2].tolist())):
+        bb, aa = b[b[:, 2] == loc], a[a[:, 2] == loc]
         dc = aa[:, 0].astype(np.float64).mean() - bb[:, 0].astype(np.float64).mean()
         dr = aa[:, 1].astype(np.float64).mean() - bb[:, 1].astype(np.float64).mean()
         if dr > 0:
-            out[int(x)] = 100.0 * dc / dr
-    return out
+            per_xcd.setdefault(int(loc) & 0xF, []).append(100.0 * dc / dr)
+    return {x: float(np.median(v)) for x, v in sorted(per_xcd.items())}
 
 
 def groupnorm_silu_bf16(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, workspace,

@@ -33,7 +33,7 @@ constexpr int kCalBlocks = 512, kCalThreads = 256;
 constexpr size_t kCalPatternBytes = (size_t)kCalFrags * 64 * 16;
 constexpr size_t kCalClockBytes = (size_t)kCalBlocks * 2 * sizeof(uint64_t);
 constexpr size_t kCalScratch = kCalPatternBytes + kCalClockBytes + 256;
-constexpr int kStampBlocks = 64;
+constexpr int kStampBlocks = 2048;
 
 __global__ __launch_bounds__(256) void cal_fill_kernel(uint32_t *p, int64_t words) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -150,17 +150,20 @@ hipError_t time_launches(F launch, int reps, hipStream_t s, float *ms) {
     return e;
 }
 
-// One wave per workgroup; workgroups are dealt to the XCDs round-robin, so
-// kStampBlocks / 8 of them land on each.
+// One wave per workgroup, about eight per CU, so that nearly every CU is
+// stamped by both of two launches.  The shader-clock counters of different CUs
+// are not aligned with one another, so a stamp carries its location: the XCD
+// in bits 0-3 and the SE/SH/CU fields of HW_ID (its bits 8-15) in bits 8-15.
 __global__ __launch_bounds__(64) void cal_stamp_kernel(uint64_t *out) {
     if (threadIdx.x == 0) {
-        uint32_t xcc;
+        uint32_t xcc, hw;
         asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
         const uint64_t c = __builtin_amdgcn_s_memtime();
         const uint64_t r = __builtin_amdgcn_s_memrealtime();
         out[3 * blockIdx.x] = c;
         out[3 * blockIdx.x + 1] = r;
-        out[3 * blockIdx.x + 2] = xcc & 0xFu;
+        out[3 * blockIdx.x + 2] = (uint64_t)((xcc & 0xFu) | (hw & 0xFF00u));
     }
 }
 

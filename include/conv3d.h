@@ -255,15 +255,18 @@ conv3d_status conv3d_calibrate_hbm(const void *src, void *dst, size_t bytes, dou
 /*
  * Measurement aid, not on the convolution path: the mean shader clock over
  * work enqueued between two stamps.  conv3d_clock_stamp enqueues on `stream`
- * a tiny kernel (64 one-wave workgroups, dealt round-robin to the 8 XCDs);
- * workgroup b writes three uint64 at out[3b..3b+2]: the shader-clock counter
- * (s_memtime, which runs at the shader clock), the 100 MHz reference counter
- * (s_memrealtime) and the id of the XCD it ran on.  For each XCD, the change
- * of its mean shader-clock counter between two stamps over the change of its
- * mean reference counter, times 100 MHz, is that XCD's mean clock over the
- * work between them.  It neither waits nor synchronises: read `out` after the
- * stream has passed it.  out: device memory of at least
- * conv3d_clock_stamp_bytes(), 16-byte aligned, overwritten.
+ * a tiny kernel of 2048 one-wave workgroups (about eight per CU); workgroup b
+ * writes three uint64 at out[3b..3b+2]: the shader-clock counter (s_memtime,
+ * which runs at the shader clock), the 100 MHz reference counter
+ * (s_memrealtime) and where it ran: the XCD in bits 0-3 and the SE/SH/CU
+ * fields of the HW_ID register (its bits 8-15) in bits 8-15.  The shader-clock
+ * counters of different CUs are not aligned with one another, so stamps are
+ * paired by location: for a CU stamped by both launches, the change of its
+ * mean shader-clock counter over the change of its mean reference counter,
+ * times 100 MHz, is that CU's mean clock over the work between them.  It
+ * neither waits nor synchronises: read `out` after the stream has passed it.
+ * out: device memory of at least conv3d_clock_stamp_bytes(), 16-byte aligned,
+ * overwritten.
  * Errors: INVALID_ARG (null or misaligned out), WORKSPACE (too small), HIP.
  */
 size_t conv3d_clock_stamp_bytes(void);

@@ -241,7 +241,7 @@ def test_groupnorm_noalloc_without_a_device_reports_no_device():
 def test_clock_stamp_argument_checks():
     lib = c3d.load_library()
     need = c3d.conv3d_clock_stamp_bytes()
-    assert need == 64 * 3 * 8
+    assert need == 2048 * 3 * 8
     assert lib.conv3d_clock_stamp(None, need, None) == c3d.CONV3D_ERR_INVALID_ARG
     assert lib.conv3d_clock_stamp(A + 4, need, None) == c3d.CONV3D_ERR_INVALID_ARG
     assert lib.conv3d_clock_stamp(A, need - 8, None) == c3d.CONV3D_ERR_WORKSPACE
@@ -256,6 +256,22 @@ def test_sclk_between_pairs_stamps_by_xcd():
     after[:, 1] += 100_000
     got = c3d.sclk_between(before.reshape(-1), after.reshape(-1))
     assert got == {0: 1500.0, 1: 2000.0}
+
+
+def test_sclk_between_pairs_stamps_by_cu():
+    import numpy as np
+    # XCD 3 with five CUs whose shader-clock counters are far apart; every CU
+    # runs at 1600 MHz.  The two launches stamp different subsets of the CUs
+    # (CU 4 only before, CU 5 only after), so averaging the XCD's counters
+    # without pairing them by CU would be off by the offsets.
+    offset = {1: 0, 2: 7_000_000, 3: 123_456_789, 4: 5_000, 5: 40_000_000}
+    loc = lambda cu: 3 | (cu << 8)
+    before = np.array([[offset[cu] + 10 * k, 1_000 + k, loc(cu)] for cu in (1, 2, 3, 4) for k in range(2)],
+                      dtype=np.uint64)
+    after = np.array([[offset[cu] + 1_600_000 + 10 * k, 101_000 + k, loc(cu)] for cu in (1, 2, 3, 5)
+                      for k in range(3)], dtype=np.uint64)
+    got = c3d.sclk_between(before.reshape(-1), after.reshape(-1))
+    assert list(got) == [3] and abs(got[3] - 1600.0) < 0.5, got
 
 
 def test_calibration_argument_checks():

@@ -36,7 +36,11 @@ def test_clock_stamps_cover_every_xcd_and_give_a_plausible_clock():
     torch.cuda.synchronize()
     b = before.cpu().numpy().view(np.uint64).reshape(-1, 3)
     a = after.cpu().numpy().view(np.uint64).reshape(-1, 3)
-    assert sorted(set(b[:, 2].tolist())) == list(range(8)) == sorted(set(a[:, 2].tolist()))
+    assert sorted(set((b[:, 2] & 0xF).tolist())) == list(range(8)) == sorted(set((a[:, 2] & 0xF).tolist()))
+    # nearly every CU (8 XCDs x 32) is stamped both times
+    assert len(set(b[:, 2].tolist()) & set(a[:, 2].tolist())) >= 200
     mhz = c3d.sclk_between(b.reshape(-1), a.reshape(-1))
     assert sorted(mhz) == list(range(8))
     assert all(500.0 < v < 2600.0 for v in mhz.values()), mhz
+    # every XCD ran the same MFMA load: the CU-paired figures agree closely
+    assert max(mhz.values()) < 1.1 * min(mhz.values()), mhz
