@@ -41,6 +41,11 @@
 //            instruction per memory phase (5 per wave) during the current
 //            slab and waited for before the barrier that starts the next.
 // K-pieces of a split tile start and end on slab boundaries.
+//
+// Tile order.  Each XCD walks a contiguous range of tiles in blocks of 4 frames
+// x 8 tiles (ps_walk), so that the 32 tiles it runs at once share their input
+// rows in its L2; against tiles along one frame this cut the 33-frame 256x256
+// conv's time by 2.5%, mostly through a higher clock (less traffic, less power).
 #include "igemm_common.h"
 
 namespace c3d {
@@ -63,6 +68,36 @@ static_assert(kPsLds <= 160 * 1024, "LDS is 160 KiB per CU");
 // Bank swizzle of a slab row: any 16 consecutive rows read at one logical
 // chunk occupy 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int slab_swz(int row) { return (row >> 1) & 7; }
+
+// Order of the whole tiles within an XCD's range.  The 32 workgroups an XCD
+// runs at once take consecutive positions of its range; walking the frames in
+// blocks of kPsBlockT frames x kPsBlockH tiles, instead of tile after tile
+// along one frame, makes those 32 tiles share their input: per channel slice a
+// block of 4 frames x 8 rows (256-voxel rows) reads (4 + 2) x (8 + 2) frame
+// rows of input, 32 tiles along one frame 3 x (32 + 2).  Tiles are numbered
+// m-tile-major (tile = m_tile * n_tiles + n_tile) and an m-tile holds 256
+// voxels of one frame when Ho * Wo is a multiple of 256; frames are the
+// flattened (sample, frame) index.  Whole frames of the data-parallel range are
+// permuted block by block (the last block of a frame group may hold fewer
+// frames, the last block of a frame fewer tiles); the rest keep their order.
+constexpr int kPsBlockT = 4, kPsBlockH = 8;
+
+__device__ __forceinline__ int ps_walk(int s, const ConvParams &p) {
+    const int hw = p.Ho * p.Wo;
+    if (hw % kPsBM != 0 || p.dp_tiles % p.n_tiles != 0) return s;
+    const int per_frame = hw / kPsBM;
+    const int ms = s / p.n_tiles, nt = s - ms * p.n_tiles;
+    const int frames = (p.dp_tiles / p.n_tiles) / per_frame;  // whole frames of the range
+    if (ms >= frames * per_frame) return s;
+    const int f0 = ms / (kPsBlockT * per_frame) * kPsBlockT;    // first frame of the group
+    const int nf = frames - f0 < kPsBlockT ? frames - f0 : kPsBlockT;
+    const int r = ms - f0 * per_frame;                          // position in the group
+    const int blk = r / (nf * kPsBlockH);                       // block of tiles along the frame
+    const int nh = per_frame - blk * kPsBlockH < kPsBlockH ? per_frame - blk * kPsBlockH : kPsBlockH;
+    const int q = r - blk * nf * kPsBlockH;                     // position in the block
+    const int fi = q / nh, hi = q - fi * nh;
+    return ((f0 + fi) * per_frame + blk * kPsBlockH + hi) * p.n_tiles + nt;
+}
 
 __device__ __forceinline__ void ps_barrier() {
     __builtin_amdgcn_sched_barrier(0);
@@ -88,14 +123,15 @@ __global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
     const int gw = wv & 3;              // wave within the group
     const int wmi = gw, wni = grp;      // this wave's 64 voxels and 128 output channels
 
-    // Work: whole tiles in XCD-contiguous ranges, then K-pieces of the split
-    // tiles, cut on slab (3-stage) boundaries.
+    // Work: whole tiles in XCD-contiguous ranges, walked in frame blocks
+    // (ps_walk), then K-pieces of the split tiles, cut on slab (3-stage)
+    // boundaries.
     const int bid = blockIdx.x;
     int tile, it0 = 0, it1 = p.niter, slot = -1;
     if (bid < p.dp_tiles) {
         const int per = p.dp_tiles >> 3, rem = p.dp_tiles & 7;
         const int xcd = bid & 7;
-        tile = xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3);
+        tile = ps_walk(xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3), p);
     } else {
         slot = bid - p.dp_tiles;
         const int piece = slot % p.sk_pieces;
