@@ -5,7 +5,9 @@ The kernel covers kw = 3 with pw = 1, kt, kh <= 3 and output rows that tile
 Ternary inputs make every partial sum a small integer, so outputs must match
 the oracle bit for bit: every row length it takes, both temporal modes, a
 channel tail, two samples, an M tail (a last tile past the output), the K
-split, bias + residual, bf16, and the first-frame fold (kt = 1 after folding).
+split, bias + residual, bf16, the first-frame fold (kt = 1 after folding), and
+the frame-block walk of whole tiles over frame groups and blocks of every
+partial size.
 """
 import numpy as np
 import pytest
@@ -67,6 +69,26 @@ def test_slab_kernel_k_split_exact_and_equal_to_whole_tiles():
     ref, _ = oracle_full(s, x, w, b)
     assert np.array_equal(y1.astype(np.float64), ref)
     assert np.array_equal(y0, y1)
+
+
+WALK_CASES = [
+    ConvShape(2, 5, 12, 64, 32, 64),      # 3 tiles per frame, 10 frames over two samples: groups of 4, 4, 2 frames
+    ConvShape(1, 9, 16, 128, 64, 64),     # 8 tiles per frame, 9 frames: the last group holds one frame
+    ConvShape(1, 6, 4, 128, 64, 320),     # 2 tiles per frame and two column tiles: groups of 4, 2 frames
+]
+
+
+@pytest.mark.parametrize("case", range(len(WALK_CASES)))
+def test_slab_kernel_frame_block_walk_exact(case):
+    # whole tiles only, so every tile goes through the frame-block walk; ternary data, bit-exact
+    s = WALK_CASES[case]
+    x, w = ternary(s.x_shape, 400 + case), ternary(s.w_shape, 410 + case)
+    b = np.random.default_rng(420 + case).integers(-2, 3, s.cout).astype(np.float16)
+    y, info = run_conv(s, x, w, b, tile=TILE, split="0")
+    assert info.split_tiles == 0
+    ref, _ = oracle_full(s, x, w, b)
+    assert np.array_equal(y.astype(np.float64), ref), "%d of %d outputs differ" % (
+        int((y.astype(np.float64) != ref).sum()), y.size)
 
 
 def test_slab_kernel_random_with_bias_and_residual_within_bound():
