@@ -1,6 +1,6 @@
 // Measurement aids: the MFMA and HBM ceilings of the machine the library runs
-// on, against which the conv (MFMA-bound) and the 1x1x1 / GroupNorm kernels
-// (HBM-bound) are judged next to the published peaks.  Not on the conv path.
+// on, a second yardstick beside the published peaks for the conv (MFMA-bound)
+// and the 1x1x1 / GroupNorm kernels (HBM-bound).  Not on the conv path.
 //
 //  * MFMA: every CU runs independent v_mfma_f32_32x32x16_f16 chains, 8 waves
 //    per CU, on fp16 operands from a fixed pseudo-random pattern, rotated
