@@ -61,8 +61,8 @@ struct TileCfg {
 const TileCfg *tile_table(int *count);
 
 // The row-slab ping-pong kernel (conv3d_ps.hip): 256 voxels x 256 channels x
-// 64, for kw = 3 with pw = 1, kt, kh <= 3, and output rows that tile 256-voxel
-// blocks (Wo a multiple of 32 dividing 256, or a multiple of 256).
+// 64, for kw = 3 with pw = 1, kt, kh <= 3, and output rows a multiple of 32
+// voxels long.
 bool ps_supported(const ConvParams &q);
 template <bool TAIL>
 hipError_t launch_ps(const ConvParams &p, hipStream_t s);

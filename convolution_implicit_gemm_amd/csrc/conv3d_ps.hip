@@ -5,17 +5,19 @@
 // implicit-GEMM lowering of the Draw Things engineering feed's post on the
 // Codex-written Metal conv3d shaders).  This kernel covers the common video-VAE
 // shape, 3 taps along w with one voxel of zero padding (kw = 3, pw = 1), output
-// rows a multiple of 32 voxels long that tile 256-voxel blocks (Wo | 256 or
-// 256 | Wo), at most 3 taps along t and h.  Tile: 256 voxels x 256 output
-// channels, 64 input channels per K-stage, 8 waves.
+// rows a multiple of 32 voxels long, at most 3 taps along t and h.  Tile: 256
+// voxels x 256 output channels, 64 input channels per K-stage, 8 waves.
 //
-// Row slabs.  A tile's 256 output voxels are R = 256 / L segments of L =
-// min(Wo, 256) voxels, each inside one output row.  For one channel slice and
-// one (tau, r) the three taps s = 0, 1, 2 read, per segment, the same input
-// row shifted by one voxel: input voxels w0 - 1 .. w0 + L.  So the kernel
-// loads that slab (R * (L + 2) voxels x 64 channels, zero where it leaves the
-// frame) into LDS once, and the three K-stages (tau, r, s) read their MFMA
-// B-fragments from it at slab row (segment * (L + 2) + v + s).  Against one
+// Row slabs.  A tile's 256 output voxels fall into segments, each the part of
+// one output row inside the tile: the first starts where the tile starts (at a
+// multiple of 32 within its row), the others at row starts.  For one channel
+// slice and one (tau, r) the three taps s = 0, 1, 2 read, per segment, the same
+// input row shifted by one voxel: input voxels w0 - 1 .. w0 + len.  So the
+// kernel loads that slab (256 + 2 x segments voxels x 64 channels, zero where
+// it leaves the frame) into LDS once, and the three K-stages (tau, r, s) read
+// their MFMA B-fragments from it at slab row v + 2 x segment(v) + s for tile
+// voxel v.  A 32-voxel fragment never crosses a row end, since rows are a
+// multiple of 32 voxels long and tiles start at multiples of 256.  Against one
 // activation tile per stage this loads 40 instead of 96 1-KiB instructions per
 // three stages and computes the gather offsets once per slab instead of once
 // per stage.  The slab rows carry their own bank swizzle, chunk ^ ((row >> 1)
@@ -58,7 +60,7 @@ constexpr int kPsWM = 64, kPsWN = 128;
 constexpr int kPsTM = kPsWM / 32, kPsTN = kPsWN / 32;
 constexpr int kPsRB = kPsBK * 2;                  // bytes per LDS row
 constexpr int kPsWHalf = 128 * kPsRB;             // one group's half of one weight stage: 16 KiB
-constexpr int kPsSlabRows = 320;                  // 40 load instructions; R * (L + 2) <= 264 rows are used
+constexpr int kPsSlabRows = 320;                  // 40 load instructions; at most 256 + 2 x 9 rows are used
 constexpr int kPsSlabBytes = kPsSlabRows * kPsRB; // 40 KiB
 constexpr int kPsSlabBase = 4 * kPsWHalf;         // weights: [group][buffer] halves, then the 2 slabs
 constexpr int kPsLds = kPsSlabBase + 2 * kPsSlabBytes;  // 144 KiB
@@ -147,8 +149,10 @@ __global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
     const int T = p.T, H = p.H, W = p.W, Cin = p.Cin;
     const int HW = H * W;
     const int M = (int)p.M;
-    const int L = p.Wo < kPsBM ? p.Wo : kPsBM;  // voxels per segment
-    const int LS = L + 2;                       // slab rows per segment
+    // segments: the first holds tile voxels [0, len0), the k-th (k >= 1)
+    // [len0 + (k - 1) Wo, len0 + k Wo) clipped to the tile
+    const int len0 = p.Wo - m0 % p.Wo < kPsBM ? p.Wo - m0 % p.Wo : kPsBM;
+    auto seg_of = [&](int v) { return v < len0 ? 0 : 1 + (v - len0) / p.Wo; };
 
     auto vb_of = [&](int m, int &to, int &ho, int &wo) {
         wo = m % p.Wo;
@@ -185,12 +189,16 @@ __global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
 #pragma unroll
     for (int j = 0; j < kPsSlabSlots; ++j) {
         const int row = (j * 8 + wv) * 8 + lrow;
-        const int seg = row / LS, u = row - seg * LS;
+        // this slab row's segment, its position u in the segment's rows (u = 0:
+        // the voxel left of the segment's first) and the segment's first voxel
+        const int seg = row < len0 + 2 ? 0 : 1 + (row - len0 - 2) / (p.Wo + 2);
+        const int u = seg == 0 ? row : (row - len0 - 2) - (seg - 1) * (p.Wo + 2);
+        const int vs = seg == 0 ? 0 : len0 + (seg - 1) * p.Wo;
         const int chunk = lchunk ^ slab_swz(row);
         s_c8[j] = chunk * 8;
         s_tb0[j] = s_d1[j] = s_d2[j] = s_ok[j] = 0;
-        const int m = m0 + seg * L;             // first voxel of the segment
-        if (seg * L < kPsBM && m < M) {
+        const int m = m0 + vs;                  // first voxel of the segment
+        if (vs < kPsBM && m < M) {
             int to, ho, wo;
             const int vb = vb_of(m, to, ho, wo);
             const int wi = wo + u - p.pw;       // input column of this slab row
@@ -279,7 +287,7 @@ __global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
 
     // ---- fragment offsets.  Weights (MFMA A): rows 32i + lane%32 of the
     // group's half.  Slab (MFMA B), fragment j at shift s: slab row
-    // seg * LS + v + lane%32 + s for the fragment's segment seg and start v.
+    // v + lane%32 + 2 seg + s for the fragment's start v and segment seg.
     const int rrow = lane & 31, rhi = lane >> 5;
     int koff_w[4];
 #pragma unroll
@@ -288,10 +296,10 @@ __global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
 #pragma unroll
     for (int j = 0; j < kPsTM; ++j) {
         const int v = wmi * kPsWM + j * 32;
-        const int seg = v / L, v0 = v - seg * L;
+        const int seg = seg_of(v);
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
-            const int row = seg * LS + v0 + rrow + s;
+            const int row = v + rrow + 2 * seg + s;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
                 koff_b[j][s][kk] = kPsSlabBase + row * kPsRB + (((2 * kk + rhi) ^ slab_swz(row)) * 16);
@@ -414,10 +422,8 @@ __global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
 }
 
 bool ps_supported(const ConvParams &q) {
-    const int L = q.Wo < kPsBM ? q.Wo : kPsBM;
-    const int R = kPsBM / L;
-    return q.kw == 3 && q.pw == 1 && q.kt <= 3 && q.kh <= 3 && q.Wo % 32 == 0 &&
-           (q.Wo % kPsBM == 0 || kPsBM % q.Wo == 0) && R * (L + 2) <= kPsSlabRows;
+    // at most 256 / 32 + 1 segments per tile: 256 + 2 x 9 slab rows
+    return q.kw == 3 && q.pw == 1 && q.kt <= 3 && q.kh <= 3 && q.Wo % 32 == 0 && q.Wo == q.W;
 }
 
 template <bool TAIL>

@@ -1,7 +1,8 @@
 """GPU parity of the row-slab kernel (m256n256k64ps) against the fp64 oracle.
 
-The kernel covers kw = 3 with pw = 1, kt, kh <= 3 and output rows that tile
-256-voxel blocks (Wo a multiple of 32 dividing 256, or a multiple of 256).
+The kernel covers kw = 3 with pw = 1, kt, kh <= 3 and output rows a multiple
+of 32 voxels long (tiles of 256 voxels may start inside a row and cross rows,
+frames and samples).
 Ternary inputs make every partial sum a small integer, so outputs must match
 the oracle bit for bit: every row length it takes, both temporal modes, a
 channel tail, two samples, an M tail (a last tile past the output), the K
@@ -42,6 +43,12 @@ SLAB_CASES = [
     ConvShape(1, 3, 3, 32, 64, 64, pad_t_front=2, tmode=Z),                # M = 288: a partial last tile
     ConvShape(1, 4, 5, 64, 128, 128, kt=1, kh=3, pad_t_front=0),           # kt = 1 (a 2D conv per frame)
     ConvShape(1, 3, 5, 64, 64, 64, kt=2, kh=2, pad_t_front=1, pad_h=1),    # even extents in t and h
+    # rows that do not tile 256 voxels: tiles start inside rows, and cross rows,
+    # frames and samples
+    ConvShape(1, 3, 5, 96, 64, 64),                                        # 96-voxel rows, 480 voxels per frame
+    ConvShape(2, 3, 3, 160, 72, 64),                                       # 160-voxel rows, N = 2, channel tail
+    ConvShape(1, 2, 4, 320, 64, 128),                                      # 320-voxel rows (longer than a tile)
+    ConvShape(1, 2, 3, 224, 64, 64, tmode=Z, pad_t_front=1, pad_t_back=1),  # 224-voxel rows, symmetric zero
 ]
 
 
@@ -75,6 +82,7 @@ WALK_CASES = [
     ConvShape(2, 5, 12, 64, 32, 64),      # 3 tiles per frame, 10 frames over two samples: groups of 4, 4, 2 frames
     ConvShape(1, 9, 16, 128, 64, 64),     # 8 tiles per frame, 9 frames: the last group holds one frame
     ConvShape(1, 6, 4, 128, 64, 320),     # 2 tiles per frame and two column tiles: groups of 4, 2 frames
+    ConvShape(1, 6, 8, 96, 64, 64),       # 96-voxel rows, 3 tiles per frame: tiles start inside rows
 ]
 
 
@@ -127,7 +135,7 @@ def test_slab_kernel_first_frame_fold_exact(tmode):
 
 
 def test_slab_kernel_rejects_shapes_it_does_not_cover():
-    # rows of 48 voxels neither divide nor are a multiple of 256: forcing the tile plans nothing
+    # rows of 48 voxels are not a multiple of 32: forcing the tile plans nothing
     import os
     from helpers import conv_desc, forced_tile
     with forced_tile(TILE):
