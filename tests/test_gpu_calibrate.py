@@ -31,7 +31,7 @@ def test_clock_stamps_cover_every_xcd_and_give_a_plausible_clock():
     after = torch.zeros_like(before)
     scratch = torch.empty(c3d.conv3d_calibrate_scratch_bytes(), dtype=torch.uint8, device="cuda:0")
     c3d.conv3d_clock_stamp(before)
-    c3d.conv3d_calibrate_mfma(scratch)   # a few ms of MFMA load between the stamps (synchronises)
+    _, cal_mhz = c3d.conv3d_calibrate_mfma(scratch)   # a few ms of MFMA load between the stamps (synchronises)
     c3d.conv3d_clock_stamp(after)
     torch.cuda.synchronize()
     b = before.cpu().numpy().view(np.uint64).reshape(-1, 3)
@@ -42,5 +42,10 @@ def test_clock_stamps_cover_every_xcd_and_give_a_plausible_clock():
     mhz = c3d.sclk_between(b.reshape(-1), a.reshape(-1))
     assert sorted(mhz) == list(range(8))
     assert all(500.0 < v < 2600.0 for v in mhz.values()), mhz
-    # every XCD ran the same MFMA load: the CU-paired figures agree closely
-    assert max(mhz.values()) < 1.1 * min(mhz.values()), mhz
+    # The XCDs clock independently (up to about 12% apart under this load), but
+    # CU-paired figures stay close together and close to the clock the
+    # calibration kernel measures inside its own waves; stamps paired across
+    # CUs had given figures a factor of two apart
+    assert max(mhz.values()) < 1.3 * min(mhz.values()), mhz
+    mean = sum(mhz.values()) / len(mhz)
+    assert abs(mean - cal_mhz) < 0.15 * cal_mhz, (mhz, cal_mhz)
