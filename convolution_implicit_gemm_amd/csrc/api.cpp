@@ -75,6 +75,21 @@ conv3d_status check_device() {
     return CONV3D_OK;
 }
 
+// Compute units of the current device, cached per device (the dynamic tile
+// schedule launches one workgroup per CU).
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kCUs;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = kCUs;
+        g_cu_count[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
@@ -97,6 +112,7 @@ constexpr double kLaunchSeconds = 4e-6;
 constexpr size_t kMaxSplitWorkspace = (size_t)256 << 20;
 constexpr double kCopyBytesPerSec = 5.5e12;  // device-to-device copy, read + write bytes
 constexpr size_t kMaxChunkCopy = (size_t)512 << 20;  // largest [x_prev; x] copy a chunk plan makes
+constexpr int kDynamicWaves = 8;  // whole-tile waves from which the slab kernel schedules dynamically
 
 // Cost model: each CU runs ceil(tiles/CUs) whole tiles at the configuration's
 // measured rate; a split run fills the last wave with K-pieces instead and
@@ -135,6 +151,8 @@ struct conv3d_plan_s {
     int fold_lo, fold_hi;
     int64_t fold_khwc;
     size_t ws_fold;       // bytes of folded weights at the start of the workspace
+    size_t ws_queue = 0;  // dynamic tile schedule: offset of its counters in the workspace
+    bool dynamic = false;
     size_t ws_bytes;
     int64_t x_elems, w_elems, y_elems;
     double flops;
@@ -318,6 +336,21 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
         q.sk_tiles = 0;
         p->ws_bytes = p->ws_fold;
     }
+    // Dynamic tile schedule (the XCDs run at different clocks; with equal
+    // shares the slowest decides) for long grids, where it pays for its
+    // counters' reset launch and the per-tile grab: at least kDynamicWaves
+    // waves of whole tiles.  CONV3D_DYNAMIC=0/1 forbids/forces it.
+    q.queue = nullptr;
+    if (!p->streaming && best->dynamic) {
+        const char *dyn = getenv("CONV3D_DYNAMIC");
+        p->dynamic = dyn && *dyn == '1' ? true
+                     : dyn && *dyn == '0' ? false
+                                          : q.dp_tiles >= (int64_t)kDynamicWaves * kCUs;
+        if (p->dynamic) {
+            p->ws_queue = (p->ws_bytes + 255) & ~(size_t)255;
+            p->ws_bytes = p->ws_queue + c3d::ps_queue_bytes();
+        }
+    }
 
     *out = p;
     *workspace_bytes = p->ws_bytes;
@@ -362,6 +395,7 @@ conv3d_status conv3d_plan_query(conv3d_plan_t p, conv3d_plan_info *info) {
     info->stages = p->tile->stages;
     info->threads = p->tile->threads;
     info->grid = p->prm.dp_tiles + (int64_t)p->prm.sk_tiles * p->prm.sk_pieces;
+    if (p->dynamic && info->grid > kCUs) info->grid = kCUs;  // one workgroup per CU takes the units
     info->split_tiles = p->prm.sk_tiles;
     info->split_pieces = p->prm.sk_tiles ? p->prm.sk_pieces : 0;
     snprintf(info->kernel_name, sizeof(info->kernel_name), "conv3d_igemm_%s%s", p->tile->name,
@@ -407,6 +441,10 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
     q.res = has_res ? static_cast<const _Float16 *>(residual) : nullptr;
     q.y = static_cast<_Float16 *>(y);
     if (q.sk_tiles) q.partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + p->ws_fold);
+    if (p->dynamic) {
+        q.queue = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + p->ws_queue);
+        q.grid_cap = cu_count();
+    }
     if (p->path == CONV3D_PATH_T1_FOLD) {
         _Float16 *w2 = static_cast<_Float16 *>(workspace);
         hipError_t e = c3d::launch_fold_taps(q.w, w2, p->d.c_out, p->d.kt, p->fold_khwc, p->fold_lo, p->fold_hi,

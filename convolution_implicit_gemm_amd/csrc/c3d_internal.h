@@ -34,6 +34,8 @@ struct ConvParams {
     int64_t M;             // N*To*Ho*Wo, below 2^30
     int64_t tiles;         // m_tiles*n_tiles
     int32_t bf16;          // elements are bf16 (else fp16)
+    uint32_t *queue;       // counters of the dynamic tile schedule (workspace), or null: static
+    int32_t grid_cap;      // dynamic schedule: at most this many workgroups (one per CU)
 };
 
 // Most K-pieces a split tile may be cut into (the fixup kernel loads them all
@@ -56,6 +58,7 @@ struct TileCfg {
     ConvLaunchFn launch_tail;  // any Cin % 8 == 0 (channel tail zero-filled per tap)
     ConvLaunchFn launch_fixup; // sums the K-pieces of the split tiles, then the epilogue
     bool (*supported)(const ConvParams &q);  // null: every shape; else the shapes it runs
+    bool dynamic;              // launch_full/tail also run the dynamic schedule (ConvParams::queue)
 };
 
 const TileCfg *tile_table(int *count);
@@ -64,6 +67,8 @@ const TileCfg *tile_table(int *count);
 // 64, for kw = 3 with pw = 1, kt, kh <= 3, and output rows a multiple of 32
 // voxels long.
 bool ps_supported(const ConvParams &q);
+// Bytes of workspace the dynamic schedule of the slab kernel needs for its counters.
+size_t ps_queue_bytes();
 template <bool TAIL>
 hipError_t launch_ps(const ConvParams &p, hipStream_t s);
 

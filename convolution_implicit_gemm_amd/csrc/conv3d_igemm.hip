@@ -500,7 +500,7 @@ hipError_t launch_fixup(const ConvParams &p, hipStream_t s) {
 #define C3D_TILE(NAME, BM, BN, BK, WM, WN, ST, AST, RATE)                                            \
     {NAME, BM, BN, BK, ST, (BM / WM) * (BN / WN) * 64, (size_t)((ST) * (BN) + (AST) * (BM)) * (BK) * 2, \
      RATE, launch_igemm<BM, BN, BK, WM, WN, ST, AST, false>, launch_igemm<BM, BN, BK, WM, WN, ST, AST, true>, \
-     launch_fixup<BM, BN, WM, WN>, nullptr}
+     launch_fixup<BM, BN, WM, WN>, nullptr, false}
 
 static const TileCfg k_tiles[] = {
     C3D_TILE("m256n256k64s2w4", 256, 256, 64, 128, 128, 2, 2, 0.82),
@@ -515,7 +515,7 @@ static const TileCfg k_tiles[] = {
     // row slabs + ping-pong (conv3d_ps.hip): 144 KiB of LDS, one workgroup per
     // CU; 5-6% faster than m256n256k64s2a3w8 on the three large causal convs
     {"m256n256k64ps", 256, 256, 64, 2, 512, (size_t)144 * 1024, 1.055, launch_ps<false>, launch_ps<true>,
-     launch_fixup<256, 256, 64, 128>, ps_supported},
+     launch_fixup<256, 256, 64, 128>, ps_supported, true},
 };
 
 int64_t tile_window_voxels(const ConvParams &q, int bm) {

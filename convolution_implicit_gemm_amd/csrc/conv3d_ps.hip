@@ -65,6 +65,7 @@ constexpr int kPsSlabBytes = kPsSlabRows * kPsRB; // 40 KiB
 constexpr int kPsSlabBase = 4 * kPsWHalf;         // weights: [group][buffer] halves, then the 2 slabs
 constexpr int kPsLds = kPsSlabBase + 2 * kPsSlabBytes;  // 144 KiB
 constexpr int kPsSlabSlots = kPsSlabRows / 8 / 8;       // slab load instructions per wave: 5
+constexpr int kPsQueueWords = 16;                       // counters of the dynamic schedule (9 used)
 static_assert(kPsLds <= 160 * 1024, "LDS is 160 KiB per CU");
 
 // Bank swizzle of a slab row: any 16 consecutive rows read at one logical
@@ -115,33 +116,37 @@ __device__ __forceinline__ void ps_wait_loads() {
 
 }  // namespace
 
-template <bool TAIL, typename E>
-__global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem[kPsLds];
-
-    const int lane = threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int grp = wv >> 2;            // waves 0-3 and 4-7: one of each per SIMD
-    const int gw = wv & 3;              // wave within the group
-    const int wmi = gw, wni = grp;      // this wave's 64 voxels and 128 output channels
-
-    // Work: whole tiles in XCD-contiguous ranges, walked in frame blocks
-    // (ps_walk), then K-pieces of the split tiles, cut on slab (3-stage)
-    // boundaries.
-    const int bid = blockIdx.x;
-    int tile, it0 = 0, it1 = p.niter, slot = -1;
-    if (bid < p.dp_tiles) {
-        const int per = p.dp_tiles >> 3, rem = p.dp_tiles & 7;
-        const int xcd = bid & 7;
-        tile = ps_walk(xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3), p);
+// Work units: u in [0, dp_tiles) is the u-th whole tile of the XCD-contiguous
+// ranges (its tile from ps_walk); u >= dp_tiles is K-piece u - dp_tiles of the
+// split tiles, cut on slab (3-stage) boundaries.
+__device__ __forceinline__ void ps_unit_of(const ConvParams &p, int u, int &tile, int &it0, int &it1, int &slot) {
+    it0 = 0;
+    it1 = p.niter;
+    slot = -1;
+    if (u < p.dp_tiles) {
+        tile = ps_walk(u, p);
     } else {
-        slot = bid - p.dp_tiles;
+        slot = u - p.dp_tiles;
         const int piece = slot % p.sk_pieces;
         tile = p.dp_tiles + slot / p.sk_pieces;
         const int nslab = p.niter / 3;
         it0 = 3 * (int)((int64_t)nslab * piece / p.sk_pieces);
         it1 = 3 * (int)((int64_t)nslab * (piece + 1) / p.sk_pieces);
     }
+}
+
+// One work unit: K-stages [it0, it1) of one tile, then its epilogue (slot < 0)
+// or its fp32 partial (slot >= 0).  Every wave of the workgroup calls it with
+// the same unit.
+template <bool TAIL, typename E>
+__device__ __forceinline__ void ps_unit(const ConvParams &p, char *smem, const int tile, const int it0,
+                                        const int it1, const int slot) {
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wv >> 2;            // waves 0-3 and 4-7: one of each per SIMD
+    const int gw = wv & 3;              // wave within the group
+    const int wmi = gw, wni = grp;      // this wave's 64 voxels and 128 output channels
+
     const int mt = tile / p.n_tiles, nt = tile - mt * p.n_tiles;
     const int m0 = mt * kPsBM;
     const int n0 = nt * kPsBN;
@@ -421,6 +426,79 @@ __global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
     store_tile<E, kPsTN, kPsTM, kPsWN, kPsWM>(p, acc, m0, kPsBM, n0, wmi, wni, rrow, rhi);
 }
 
+// Static schedule: one workgroup per work unit.  Workgroups are dealt to the
+// XCDs in turn (workgroup b to XCD b mod 8), so XCD x runs the units of the
+// x-th contiguous range.
+template <bool TAIL, typename E>
+__global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[kPsLds];
+    const int bid = blockIdx.x;
+    int u = bid;
+    if (bid < p.dp_tiles) {
+        const int per = p.dp_tiles >> 3, rem = p.dp_tiles & 7;
+        const int xcd = bid & 7;
+        u = xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3);
+    }
+    int tile, it0, it1, slot;
+    ps_unit_of(p, u, tile, it0, it1, slot);
+    ps_unit<TAIL, E>(p, smem, tile, it0, it1, slot);
+}
+
+// Dynamic schedule, for long grids: the XCDs run at different clocks, and with
+// the static one the XCD with the slowest ends last while the others idle.
+// One workgroup per CU takes units until none is left: the whole tiles of its
+// own XCD's range first (in walk order), then those of the other XCDs' ranges,
+// then the K-pieces.  p.queue holds 9 counters (one per range, one for the
+// K-pieces), zero at launch; a counter past its range's end means the range
+// is done.
+__device__ __forceinline__ int ps_grab(const ConvParams &p) {
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    const int per = p.dp_tiles >> 3, rem = p.dp_tiles & 7;
+    for (int k = 0; k < 8; ++k) {
+        const int q = (int)((xcc + (uint32_t)k) & 7u);
+        const int len = per + (q < rem ? 1 : 0);
+        if (len == 0) continue;
+        const unsigned i = atomicAdd(p.queue + q, 1u);
+        if ((int)i < len) return q * per + (q < rem ? q : rem) + (int)i;
+    }
+    const int pieces = p.sk_tiles * p.sk_pieces;
+    if (pieces > 0) {
+        const unsigned i = atomicAdd(p.queue + 8, 1u);
+        if ((int)i < pieces) return p.dp_tiles + (int)i;
+    }
+    return -1;
+}
+
+template <bool TAIL, typename E>
+__global__ __launch_bounds__(kPsThreads) void conv3d_ps_dyn_kernel(ConvParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[kPsLds + 256];
+    int *s_unit = reinterpret_cast<int *>(smem + kPsLds);
+    // thread 0 takes the next unit while the workgroup runs the current one
+    int next = 0;
+    if (threadIdx.x == 0) next = ps_grab(p);
+    for (;;) {
+        if (threadIdx.x == 0) *s_unit = next;
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        const int u = __builtin_amdgcn_readfirstlane(*s_unit);
+        // every wave has read the unit before thread 0 may write the next one
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if (u < 0) break;
+        if (threadIdx.x == 0) next = ps_grab(p);
+        int tile, it0, it1, slot;
+        ps_unit_of(p, u, tile, it0, it1, slot);
+        ps_unit<TAIL, E>(p, smem, tile, it0, it1, slot);
+    }
+}
+
+__global__ void ps_queue_zero(uint32_t *queue) {
+    if (threadIdx.x < kPsQueueWords) queue[threadIdx.x] = 0u;
+}
+
 bool ps_supported(const ConvParams &q) {
     // at most 256 / 32 + 1 segments per tile: 256 + 2 x 9 slab rows
     return q.kw == 3 && q.pw == 1 && q.kt <= 3 && q.kh <= 3 && q.Wo % 32 == 0 && q.Wo == q.W;
@@ -428,13 +506,24 @@ bool ps_supported(const ConvParams &q) {
 
 template <bool TAIL>
 hipError_t launch_ps(const ConvParams &p, hipStream_t s) {
-    const unsigned grid = (unsigned)(p.dp_tiles + p.sk_tiles * p.sk_pieces);
+    const int units = p.dp_tiles + p.sk_tiles * p.sk_pieces;
+    if (p.queue) {
+        hipLaunchKernelGGL(ps_queue_zero, dim3(1), dim3(64), 0, s, p.queue);
+        const unsigned grid = (unsigned)(units < p.grid_cap ? units : p.grid_cap);
+        if (p.bf16)
+            hipLaunchKernelGGL((conv3d_ps_dyn_kernel<TAIL, __bf16>), dim3(grid), dim3(kPsThreads), 0, s, p);
+        else
+            hipLaunchKernelGGL((conv3d_ps_dyn_kernel<TAIL, _Float16>), dim3(grid), dim3(kPsThreads), 0, s, p);
+        return hipGetLastError();
+    }
     if (p.bf16)
-        hipLaunchKernelGGL((conv3d_ps_kernel<TAIL, __bf16>), dim3(grid), dim3(kPsThreads), 0, s, p);
+        hipLaunchKernelGGL((conv3d_ps_kernel<TAIL, __bf16>), dim3((unsigned)units), dim3(kPsThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((conv3d_ps_kernel<TAIL, _Float16>), dim3(grid), dim3(kPsThreads), 0, s, p);
+        hipLaunchKernelGGL((conv3d_ps_kernel<TAIL, _Float16>), dim3((unsigned)units), dim3(kPsThreads), 0, s, p);
     return hipGetLastError();
 }
+
+size_t ps_queue_bytes() { return kPsQueueWords * sizeof(uint32_t); }
 
 template hipError_t launch_ps<false>(const ConvParams &p, hipStream_t s);
 template hipError_t launch_ps<true>(const ConvParams &p, hipStream_t s);

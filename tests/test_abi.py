@@ -129,6 +129,33 @@ def test_plan_paths_and_sizes():
     assert pw.path == c3d.CONV3D_PATH_POINTWISE and pw.gemm_k == 512
 
 
+def test_dynamic_tile_schedule_planning():
+    # the 33-frame 256x256 512->256 conv: 33 waves of whole slab-kernel tiles,
+    # scheduled dynamically (one workgroup per CU); its counters take 64 bytes
+    # of workspace
+    big = dict(t=33, h=256, w=256, c_out=256)
+    p = c3d.conv3d_plan(desc(**big))
+    i = p.info()
+    assert i.kernel_name.decode() == "conv3d_igemm_m256n256k64ps" and i.split_tiles == 0
+    assert i.grid == 256 and p.workspace_bytes == 64
+    os.environ["CONV3D_DYNAMIC"] = "0"
+    try:
+        p0 = c3d.conv3d_plan(desc(**big))
+        assert p0.info().grid == 8448 and p0.workspace_bytes == 0
+    finally:
+        del os.environ["CONV3D_DYNAMIC"]
+    # a short grid keeps one workgroup per tile; forcing the schedule adds the counters
+    # after the split partials
+    ps = c3d.conv3d_plan(desc())
+    assert ps.info().grid > 256 and ps.workspace_bytes % 256 == 0
+    os.environ["CONV3D_DYNAMIC"] = "1"
+    try:
+        pf = c3d.conv3d_plan(desc())
+        assert pf.info().grid == 256 and pf.workspace_bytes == ps.workspace_bytes + 64
+    finally:
+        del os.environ["CONV3D_DYNAMIC"]
+
+
 def test_k_split_switch():
     os.environ["CONV3D_STREAMK"] = "0"
     try:

@@ -127,3 +127,24 @@ def test_bf16_conv_and_fold_graph_replays_equal_eager():
         c3d.conv3d_forward(plan, x, w, b, None, y_eager, ws_eager)
         torch.cuda.synchronize()
         assert torch.equal(bits(y), bits(y_eager)), k
+
+
+def test_dynamic_tile_schedule_graph_replays_equal_eager():
+    # the slab kernel's dynamic schedule: a counter-reset kernel, then one
+    # workgroup per CU taking tiles; replays must find the counters reset
+    s = ConvShape(1, 9, 32, 128, 64, 64)
+    with forced_tile("m256n256k64ps"), env_var("CONV3D_DYNAMIC", "1"):
+        plan = c3d.conv3d_plan(conv_desc(s, c3d.CONV3D_F_BIAS))
+    info = plan.info()
+    assert info.kernel_name.decode().startswith("conv3d_igemm_m256n256k64ps") and plan.workspace_bytes > 0
+    d = workloads.conv_inputs(s, 1580)
+    x, w, b = dev(d["x"]), dev(d["w"]), dev(d["b"])
+    y, ws = torch.empty(out_dims(s), dtype=torch.float16, device="cuda:0"), workspace_for(plan)
+    g = capture(lambda: c3d.conv3d_forward(plan, x, w, b, None, y, ws))
+    y_eager, ws_eager = torch.empty_like(y), workspace_for(plan)
+    for k in range(REPLAYS):
+        x.copy_(dev(workloads.normal_f16(np.random.SeedSequence(1590 + k), s.x_shape)))
+        g.replay()
+        c3d.conv3d_forward(plan, x, w, b, None, y_eager, ws_eager)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(y), bits(y_eager)), k

@@ -99,6 +99,33 @@ def test_slab_kernel_frame_block_walk_exact(case):
         int((y.astype(np.float64) != ref).sum()), y.size)
 
 
+DYN_CASES = [
+    (ConvShape(1, 9, 16, 128, 64, 64), None),    # whole tiles over 9 frames
+    (ConvShape(2, 5, 12, 64, 40, 64), None),     # two samples, channel tail
+    (ConvShape(1, 3, 8, 128, 64, 96), "1"),      # every tile split into K-pieces
+    (ConvShape(1, 5, 16, 96, 64, 320), None),    # 96-voxel rows, two column tiles
+    (ConvShape(1, 9, 64, 128, 64, 64), "0"),     # 288 whole tiles on 256 workgroups: some take two
+]
+
+
+@pytest.mark.parametrize("case", range(len(DYN_CASES)))
+def test_slab_kernel_dynamic_schedule_equals_static(case):
+    # one workgroup per CU taking tiles (and K-pieces) from counters: the same
+    # tiles computed the same way as one workgroup per tile, bit for bit
+    from helpers import env_var
+    s, split = DYN_CASES[case]
+    x, w = ternary(s.x_shape, 430 + case), ternary(s.w_shape, 440 + case)
+    b = np.random.default_rng(450 + case).integers(-2, 3, s.cout).astype(np.float16)
+    with env_var("CONV3D_DYNAMIC", "1"):
+        y1, i1 = run_conv(s, x, w, b, tile=TILE, split=split)
+    with env_var("CONV3D_DYNAMIC", "0"):
+        y0, i0 = run_conv(s, x, w, b, tile=TILE, split=split)
+    assert i1.grid <= 256 and (i1.split_tiles, i1.split_pieces) == (i0.split_tiles, i0.split_pieces)
+    ref, _ = oracle_full(s, x, w, b)
+    assert np.array_equal(y0.astype(np.float64), ref)
+    assert np.array_equal(y1, y0)
+
+
 def test_slab_kernel_random_with_bias_and_residual_within_bound():
     s = ConvShape(1, 5, 16, 128, 256, 256)
     d = workloads.conv_inputs(s, 370)
