@@ -126,6 +126,38 @@ def test_slab_kernel_dynamic_schedule_equals_static(case):
     assert np.array_equal(y1, y0)
 
 
+def test_slab_kernel_dynamic_schedule_bf16_exact():
+    # the bf16 instantiation of the dynamic kernel, whole tiles and K-pieces
+    from helpers import env_var
+    s = ConvShape(1, 5, 16, 128, 64, 64)
+    x = workloads.ternary_f16(np.random.SeedSequence(460), s.x_shape)
+    w = workloads.ternary_f16(np.random.SeedSequence(461), s.w_shape)
+    to_bf = lambda a: (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    with env_var("CONV3D_DYNAMIC", "1"):
+        y1, i1 = run_conv(s, to_bf(x), to_bf(w), tile=TILE, split="1")
+    assert i1.grid <= 256 and i1.split_tiles > 0
+    ref, _ = oracle_full(s, x, w)
+    got = (y1.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(got, ref)
+
+
+def test_slab_kernel_dynamic_schedule_bias_residual_equals_static():
+    # random data with bias and residual: the dynamic schedule computes every
+    # tile and K-piece as the static one does, so the outputs agree bit for bit
+    from helpers import env_var
+    s = ConvShape(1, 9, 16, 128, 128, 64)
+    d = workloads.conv_inputs(s, 470)
+    res = workloads.normal_f16(np.random.SeedSequence(471), out_dims(s))
+    with env_var("CONV3D_DYNAMIC", "1"):
+        y1, i1 = run_conv(s, d["x"], d["w"], d["b"], res=res, tile=TILE, split="1")
+    with env_var("CONV3D_DYNAMIC", "0"):
+        y0, _ = run_conv(s, d["x"], d["w"], d["b"], res=res, tile=TILE, split="1")
+    assert i1.grid <= 256
+    assert np.array_equal(y1, y0)
+    ref, mag = oracle_full(s, d["x"], d["w"], d["b"], res)
+    assert_conv_close(y1, ref, mag, "slab kernel, dynamic schedule, bias + residual")
+
+
 def test_slab_kernel_random_with_bias_and_residual_within_bound():
     s = ConvShape(1, 5, 16, 128, 256, 256)
     d = workloads.conv_inputs(s, 370)
