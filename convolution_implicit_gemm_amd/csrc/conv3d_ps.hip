@@ -114,6 +114,91 @@ __device__ __forceinline__ void ps_wait_loads() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// 16-byte buffer store (eight 16-bit values); out-of-range stores are dropped.
+__device__ __forceinline__ void store16(buf_rsrc r, uint32_t off, half8_t v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+#else
+    (void)r;
+    (void)off;
+    (void)v;
+#endif
+}
+
+// Epilogue of one tile through LDS: + bias (+ residual) in fp32, one RNE
+// rounding, then the 256 x 256 result in LDS and out in whole rows.  Straight
+// from the MFMA fragments each store instruction would write 16 bytes into
+// each of 32 output rows, 32 partial cache lines; staged, it writes two rows'
+// 512 contiguous bytes.  LDS row v (tile voxel v) holds the tile's 256
+// channels; 16-byte chunk c sits at chunk c ^ (v & 31), so the fragment
+// accesses (32 rows at one chunk) and the row accesses (one row, 32 chunks)
+// both spread over all banks.  The residual comes in the same way, whole rows
+// into the same layout, and each lane replaces its residual values by its
+// results in place.  Every LDS buffer of the K loop is free here.
+template <typename E>
+__device__ __forceinline__ void ps_store_tile(const ConvParams &p, const f32x16 (&acc)[kPsTN][kPsTM], char *smem,
+                                              int m0, int n0, int wmi, int wni, int rrow, int rhi, int lane,
+                                              int wv) {
+    const int M = (int)p.M;
+    const int rows = M - m0 < kPsBM ? M - m0 : kPsBM;
+    const uint32_t tile_bytes = (uint32_t)rows * (uint32_t)p.Cout * 2u;
+    const buf_rsrc ry = make_rsrc(p.y + (int64_t)m0 * p.Cout, tile_bytes);
+    const buf_rsrc rb = make_rsrc(p.bias ? p.bias : p.y, p.bias ? (uint32_t)p.Cout * 2u : 0u);
+    // row accesses: wave wv takes tile voxels 32 wv .. 32 wv + 31, two per
+    // instruction, lane l chunk l % 32 of its voxel
+    const int rc = lane & 31;
+    auto row_v = [&](int k) { return wv * 32 + 2 * k + (lane >> 5); };
+    auto row_off = [&](int v, int c) {
+        const int co = n0 + 8 * c;
+        return co < p.Cout ? ((uint32_t)v * (uint32_t)p.Cout + (uint32_t)co) * 2u : kOOB;
+    };
+    const bool has_res = p.res != nullptr;
+    if (has_res) {
+        // LDS chunk rc of row v receives logical chunk rc ^ (v & 31)
+        const buf_rsrc rr = make_rsrc(p.res + (int64_t)m0 * p.Cout, tile_bytes);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int v = row_v(k);
+            dma16(rr, smem + (wv * 32 + 2 * k) * 512, row_off(v, rc ^ (v & 31)), 0u);
+        }
+        ps_wait_loads<0>();
+        ps_barrier();
+    }
+    // lane's values of fragment (i, j), register 4g + e: channel
+    // 128 wni + 32 i + 8 g + 4 rhi + e of the tile, voxel 64 wmi + 32 j + rrow
+    auto ch = [&](int i, int g) { return n0 + wni * kPsWN + i * 32 + 8 * g + 4 * rhi; };
+    half4_t bv[kPsTN][4];
+#pragma unroll
+    for (int i = 0; i < kPsTN; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bv[i][g] = load8(rb, (uint32_t)ch(i, g) * 2u);
+#pragma unroll
+    for (int i = 0; i < kPsTN; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int j = 0; j < kPsTM; ++j) {
+                const int v = wmi * kPsWM + j * 32 + rrow;
+                const int c = wni * 16 + i * 4 + g;
+                half4_t *slot = reinterpret_cast<half4_t *>(smem + v * 512 + ((c ^ (v & 31)) << 4) + rhi * 8);
+                half4_t r = {};
+                if (has_res) r = *slot;
+                half4_t h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    h[e] = from_f32<E>(acc[i][j][4 * g + e] + to_f32<E>(bv[i][g][e]) + to_f32<E>(r[e]));
+                *slot = h;
+            }
+    ps_barrier();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int v = row_v(k);
+        const half8_t h = *reinterpret_cast<const half8_t *>(smem + v * 512 + ((rc ^ (v & 31)) << 4));
+        store16(ry, row_off(v, rc), h);
+    }
+}
+
 }  // namespace
 
 // Work units: u in [0, dp_tiles) is the u-th whole tile of the XCD-contiguous
@@ -423,7 +508,9 @@ __device__ __forceinline__ void ps_unit(const ConvParams &p, char *smem, const i
                 }
         return;
     }
-    store_tile<E, kPsTN, kPsTM, kPsWN, kPsWM>(p, acc, m0, kPsBM, n0, wmi, wni, rrow, rhi);
+    // every wave is past its last LDS read and load of the K loop
+    ps_barrier();
+    ps_store_tile<E>(p, acc, smem, m0, n0, wmi, wni, rrow, rhi, lane, wv);
 }
 
 // Static schedule: one workgroup per work unit.  Workgroups are dealt to the
