@@ -276,40 +276,75 @@ __device__ __forceinline__ void ps_unit(const ConvParams &p, char *smem, const i
     // in t, and the validity of each (tau, r): bit 8 + r, bit 16 + tau.
     uint32_t s_tb0[kPsSlabSlots], s_d1[kPsSlabSlots], s_d2[kPsSlabSlots], s_ok[kPsSlabSlots];
     int s_c8[kPsSlabSlots];
+    {
+        // The 8 lanes of one slab row differ only in their 16-byte chunk, so
+        // the wave's 40 rows are worked out once, lane 8j + i taking row i of
+        // instruction j, and handed to the lanes that load them; the chunk is
+        // added after.  This runs at the head of every tile.
+        // Output coordinates of the tile's first voxel (wave-uniform): segment
+        // k >= 1 starts output row r0 + k, reached from them by carries.
+        const int wo_0 = m0 % p.Wo, r_0 = m0 / p.Wo;
+        const int ho_0 = r_0 % p.Ho, tn_0 = r_0 / p.Ho;
+        const int to_0 = tn_0 % p.To, n_0 = tn_0 / p.To;
+        const float rcp_ho = __builtin_amdgcn_rcpf((float)p.Ho), rcp_to = __builtin_amdgcn_rcpf((float)p.To);
+        // a / b for 0 <= a < 2^22: the float quotient is off by at most one
+        auto small_div = [](int a, int b, float rb) {
+            int q = (int)((float)a * rb);
+            const int r = a - q * b;
+            q += r >= b ? 1 : 0;
+            q -= r < 0 ? 1 : 0;
+            return q;
+        };
+        const int row = ((lane >> 3) * 8 + wv) * 8 + (lane & 7);  // lanes 40-63: unused rows
+        // this slab row's segment (slab rows of segment k >= 1 start at
+        // len0 + 2 + (k - 1)(Wo + 2); at most 10 segments reach slab row 319),
+        // its position u in the segment's rows (u = 0: the voxel left of the
+        // segment's first) and the segment's first voxel
+        int seg = 0;
 #pragma unroll
-    for (int j = 0; j < kPsSlabSlots; ++j) {
-        const int row = (j * 8 + wv) * 8 + lrow;
-        // this slab row's segment, its position u in the segment's rows (u = 0:
-        // the voxel left of the segment's first) and the segment's first voxel
-        const int seg = row < len0 + 2 ? 0 : 1 + (row - len0 - 2) / (p.Wo + 2);
+        for (int k = 0; k < 10; ++k) seg += row >= len0 + 2 + k * (p.Wo + 2) ? 1 : 0;
         const int u = seg == 0 ? row : (row - len0 - 2) - (seg - 1) * (p.Wo + 2);
         const int vs = seg == 0 ? 0 : len0 + (seg - 1) * p.Wo;
-        const int chunk = lchunk ^ slab_swz(row);
-        s_c8[j] = chunk * 8;
-        s_tb0[j] = s_d1[j] = s_d2[j] = s_ok[j] = 0;
+        uint32_t tb0 = 0, d1 = 0, d2 = 0, okm = 0;
         const int m = m0 + vs;                  // first voxel of the segment
         if (vs < kPsBM && m < M) {
-            int to, ho, wo;
-            const int vb = vb_of(m, to, ho, wo);
+            // output row r0 + seg: (n, to, ho) by carries from the tile's first
+            const int hs = ho_0 + seg;
+            const int ch = small_div(hs, p.Ho, rcp_ho);
+            const int ho = hs - ch * p.Ho;
+            const int ts_ = to_0 + ch;
+            const int ct = small_div(ts_, p.To, rcp_to);
+            const int to = ts_ - ct * p.To;
+            const int n = n_0 + ct;
+            const int wo = seg == 0 ? wo_0 : 0;
             const int wi = wo + u - p.pw;       // input column of this slab row
             if ((unsigned)wi < (unsigned)W) {
-                // rel: the row's voxel at (t = to - ptf, h = ho - ph), before clamping
-                const int base = vb - to * HW - ho * W - wo + wi - lo;  // voxel (n, 0, 0, wi) - lo
+                const int base = n * T * HW + wi - lo;  // voxel (n, 0, 0, wi) - lo
                 uint32_t tb[3], ok = 0;
 #pragma unroll
                 for (int tau = 0; tau < 3; ++tau) {
                     int ts = to + tau - p.ptf;
                     const bool inside = (unsigned)ts < (unsigned)T;
                     if (p.replicate) ts = ts < 0 ? 0 : (ts > T - 1 ? T - 1 : ts);
-                    tb[tau] = (uint32_t)(base + ts * HW + (ho - p.ph) * W) * (uint32_t)cin2 + (uint32_t)chunk * 16u;
+                    tb[tau] = (uint32_t)(base + ts * HW + (ho - p.ph) * W) * (uint32_t)cin2;
                     ok |= (uint32_t)(tau < p.kt && (inside || p.replicate)) << (16 + tau);
                 }
                 for (int r = 0; r < p.kh; ++r) ok |= (uint32_t)((unsigned)(ho + r - p.ph) < (unsigned)H) << (8 + r);
-                s_tb0[j] = tb[0];
-                s_d1[j] = tb[1] - tb[0];
-                s_d2[j] = tb[2] - tb[1];
-                s_ok[j] = ok;
+                tb0 = tb[0];
+                d1 = tb[1] - tb[0];
+                d2 = tb[2] - tb[1];
+                okm = ok;
             }
+        }
+#pragma unroll
+        for (int j = 0; j < kPsSlabSlots; ++j) {
+            const int src = j * 8 + lrow;
+            const int chunk = lchunk ^ slab_swz((j * 8 + wv) * 8 + lrow);
+            s_c8[j] = chunk * 8;
+            s_tb0[j] = (uint32_t)__shfl((int)tb0, src) + (uint32_t)chunk * 16u;
+            s_d1[j] = (uint32_t)__shfl((int)d1, src);
+            s_d2[j] = (uint32_t)__shfl((int)d2, src);
+            s_ok[j] = (uint32_t)__shfl((int)okm, src);
         }
     }
     // ---- weight slots: instruction q = 4j + gw of group g fills rows 8q .. 8q+7
