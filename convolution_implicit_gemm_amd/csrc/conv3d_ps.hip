@@ -126,17 +126,18 @@ __device__ __forceinline__ void store16(buf_rsrc r, uint32_t off, half8_t v) {
 #endif
 }
 
-// Epilogue of one tile through LDS: + bias (+ residual) in fp32, one RNE
-// rounding, then the 256 x 256 result in LDS and out in whole rows.  Straight
-// from the MFMA fragments each store instruction would write 16 bytes into
-// each of 32 output rows, 32 partial cache lines; staged, it writes two rows'
-// 512 contiguous bytes.  LDS row v (tile voxel v) holds the tile's 256
-// channels; 16-byte chunk c sits at chunk c ^ (v & 31), so the fragment
-// accesses (32 rows at one chunk) and the row accesses (one row, 32 chunks)
-// both spread over all banks.  The residual comes in the same way, whole rows
-// into the same layout, and each lane replaces its residual values by its
-// results in place.  Every LDS buffer of the K loop is free here.
-template <typename E>
+// Epilogue of one tile through LDS: (+ residual in fp32,) one RNE rounding,
+// then the 256 x 256 result in LDS and out in whole rows; the bias is already
+// in the accumulators.  Straight from the MFMA fragments each store
+// instruction would write 16 bytes into each of 32 output rows, 32 partial
+// cache lines; staged, it writes two rows' 512 contiguous bytes.  LDS row v
+// (tile voxel v) holds the tile's 256 channels; 16-byte chunk c sits at chunk
+// c ^ (v & 31), so the fragment accesses (32 rows at one chunk) and the row
+// accesses (one row, 32 chunks) both spread over all banks.  The residual
+// comes in the same way, whole rows into the same layout, and each lane
+// replaces its residual values by its results in place.  Every LDS buffer of
+// the K loop is free here.
+template <typename E, bool RES>
 __device__ __forceinline__ void ps_store_tile(const ConvParams &p, const f32x16 (&acc)[kPsTN][kPsTM], char *smem,
                                               int m0, int n0, int wmi, int wni, int rrow, int rhi, int lane,
                                               int wv) {
@@ -144,7 +145,6 @@ __device__ __forceinline__ void ps_store_tile(const ConvParams &p, const f32x16 
     const int rows = M - m0 < kPsBM ? M - m0 : kPsBM;
     const uint32_t tile_bytes = (uint32_t)rows * (uint32_t)p.Cout * 2u;
     const buf_rsrc ry = make_rsrc(p.y + (int64_t)m0 * p.Cout, tile_bytes);
-    const buf_rsrc rb = make_rsrc(p.bias ? p.bias : p.y, p.bias ? (uint32_t)p.Cout * 2u : 0u);
     // row accesses: wave wv takes tile voxels 32 wv .. 32 wv + 31, two per
     // instruction, lane l chunk l % 32 of its voxel
     const int rc = lane & 31;
@@ -153,8 +153,7 @@ __device__ __forceinline__ void ps_store_tile(const ConvParams &p, const f32x16 
         const int co = n0 + 8 * c;
         return co < p.Cout ? ((uint32_t)v * (uint32_t)p.Cout + (uint32_t)co) * 2u : kOOB;
     };
-    const bool has_res = p.res != nullptr;
-    if (has_res) {
+    if constexpr (RES) {
         // LDS chunk rc of row v receives logical chunk rc ^ (v & 31)
         const buf_rsrc rr = make_rsrc(p.res + (int64_t)m0 * p.Cout, tile_bytes);
 #pragma unroll
@@ -167,12 +166,6 @@ __device__ __forceinline__ void ps_store_tile(const ConvParams &p, const f32x16 
     }
     // lane's values of fragment (i, j), register 4g + e: channel
     // 128 wni + 32 i + 8 g + 4 rhi + e of the tile, voxel 64 wmi + 32 j + rrow
-    auto ch = [&](int i, int g) { return n0 + wni * kPsWN + i * 32 + 8 * g + 4 * rhi; };
-    half4_t bv[kPsTN][4];
-#pragma unroll
-    for (int i = 0; i < kPsTN; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) bv[i][g] = load8(rb, (uint32_t)ch(i, g) * 2u);
 #pragma unroll
     for (int i = 0; i < kPsTN; ++i)
 #pragma unroll
@@ -182,12 +175,15 @@ __device__ __forceinline__ void ps_store_tile(const ConvParams &p, const f32x16 
                 const int v = wmi * kPsWM + j * 32 + rrow;
                 const int c = wni * 16 + i * 4 + g;
                 half4_t *slot = reinterpret_cast<half4_t *>(smem + v * 512 + ((c ^ (v & 31)) << 4) + rhi * 8);
-                half4_t r = {};
-                if (has_res) r = *slot;
                 half4_t h;
+                if constexpr (RES) {
+                    const half4_t r = *slot;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    h[e] = from_f32<E>(acc[i][j][4 * g + e] + to_f32<E>(bv[i][g][e]) + to_f32<E>(r[e]));
+                    for (int e = 0; e < 4; ++e) h[e] = from_f32<E>(acc[i][j][4 * g + e] + to_f32<E>(r[e]));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) h[e] = from_f32<E>(acc[i][j][4 * g + e]);
+                }
                 *slot = h;
             }
     ps_barrier();
@@ -431,13 +427,23 @@ __device__ __forceinline__ void ps_unit(const ConvParams &p, char *smem, const i
         }
     }
 
+    // A whole tile's accumulators start at its bias (fetched with the first
+    // stage's loads), so that the epilogue only rounds; a K-piece's partial
+    // starts at zero and the fixup adds the bias.  Lane's register 4g + e of
+    // fragment (i, j) holds channel 128 wni + 32 i + 8 g + 4 rhi + e of the tile.
     f32x16 acc[kPsTN][kPsTM];
+    const bool bias_in_acc = slot < 0 && p.bias != nullptr;
+    half4_t bias_v[kPsTN][4];
+    if (bias_in_acc) {
+        const buf_rsrc rb = make_rsrc(p.bias, (uint32_t)p.Cout * 2u);
 #pragma unroll
-    for (int i = 0; i < kPsTN; ++i)
+        for (int i = 0; i < kPsTN; ++i)
 #pragma unroll
-        for (int j = 0; j < kPsTM; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+            for (int g = 0; g < 4; ++g) {
+                const int co = n0 + wni * kPsWN + i * 32 + 8 * g + 4 * (lane >> 5);
+                bias_v[i][g] = load8(rb, co < p.Cout ? (uint32_t)co * 2u : kOOB);
+            }
+    }
 
     half8_t af[2][kPsTN], bf[2][kPsTM];
     // fragments of k-steps KK0, KK0 + 1 at slab shift S
@@ -476,6 +482,12 @@ __device__ __forceinline__ void ps_unit(const ConvParams &p, char *smem, const i
     advance_s();
     set_slab_offsets();
     ps_wait_loads<0>();
+#pragma unroll
+    for (int i = 0; i < kPsTN; ++i)
+#pragma unroll
+        for (int j = 0; j < kPsTM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = bias_in_acc ? to_f32<E>(bias_v[i][e >> 2][e & 3]) : 0.0f;
     ps_barrier();
     if (grp) ps_barrier();  // group 1 runs one phase behind
 
@@ -545,7 +557,10 @@ __device__ __forceinline__ void ps_unit(const ConvParams &p, char *smem, const i
     }
     // every wave is past its last LDS read and load of the K loop
     ps_barrier();
-    ps_store_tile<E>(p, acc, smem, m0, n0, wmi, wni, rrow, rhi, lane, wv);
+    if (p.res)
+        ps_store_tile<E, true>(p, acc, smem, m0, n0, wmi, wni, rrow, rhi, lane, wv);
+    else
+        ps_store_tile<E, false>(p, acc, smem, m0, n0, wmi, wni, rrow, rhi, lane, wv);
 }
 
 // Static schedule: one workgroup per work unit.  Workgroups are dealt to the
