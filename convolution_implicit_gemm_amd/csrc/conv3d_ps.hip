@@ -174,23 +174,28 @@ __device__ __forceinline__ void ps_store_tile(const ConvParams &p, const f32x16 
             for (int j = 0; j < kPsTM; ++j) {
                 const int v = wmi * kPsWM + j * 32 + rrow;
                 const int c = wni * 16 + i * 4 + g;
-                half4_t *slot = reinterpret_cast<half4_t *>(smem + v * 512 + ((c ^ (v & 31)) << 4) + rhi * 8);
+                char *chunk = smem + v * 512 + ((c ^ (v & 31)) << 4);
                 half4_t h;
                 if constexpr (RES) {
-                    const half4_t r = *slot;
+                    const half4_t r = *reinterpret_cast<const half4_t *>(chunk + rhi * 8);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) h[e] = from_f32<E>(acc[i][j][4 * g + e] + to_f32<E>(r[e]));
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) h[e] = from_f32<E>(acc[i][j][4 * g + e]);
                 }
-                *slot = h;
+                // rows with bit 4 set keep their two 8-byte halves swapped, so
+                // that the 32 lanes of a half-wave (rows v and v ^ 16 share a
+                // bank group) fill all 64 banks once
+                *reinterpret_cast<half4_t *>(chunk + ((rhi ^ ((v >> 4) & 1)) << 3)) = h;
             }
     ps_barrier();
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int v = row_v(k);
-        const half8_t h = *reinterpret_cast<const half8_t *>(smem + v * 512 + ((rc ^ (v & 31)) << 4));
+        half8_t h = *reinterpret_cast<const half8_t *>(smem + v * 512 + ((rc ^ (v & 31)) << 4));
+        if (k >= 8)  // v & 16: the halves were stored swapped
+            h = __builtin_shufflevector(h, h, 4, 5, 6, 7, 0, 1, 2, 3);
         store16(ry, row_off(v, rc), h);
     }
 }
