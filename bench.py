@@ -457,12 +457,24 @@ def main():
         _, p, _ = time_steps(gn_only, 30, 6, torch, 0.3)
         p = sorted(p)
         t = p[len(p) // 2]
+        # the same calls back to back, 60 of them between one pair of events: the
+        # time per call without an event pair around each one
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(torch.cuda.current_stream())
+        for _ in range(60):
+            gn_only()
+        e1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        tb = e0.elapsed_time(e1) / 60
         sbytes = bx.numel() * 2
         kern["groupnorm_silu_256_T17"] = {"ms_median": round(t, 4), "ms_min": round(p[0], 4),
                                           "GB/s_effective_2S": round(2 * sbytes / t / 1e6, 1),
                                           "GB/s_as_implemented_3S": round(3 * sbytes / t / 1e6, 1),
                                           "frac_of_hbm_2S": round(2 * sbytes / t / 1e6 / PEAK_HBM_GBS, 3),
                                           "frac_of_hbm_3S": round(3 * sbytes / t / 1e6 / PEAK_HBM_GBS, 3),
+                                          "ms_back_to_back": round(tb, 4),
+                                          "frac_of_hbm_2S_back_to_back": round(2 * sbytes / tb / 1e6 / PEAK_HBM_GBS, 3),
+                                          "frac_of_hbm_3S_back_to_back": round(3 * sbytes / tb / 1e6 / PEAK_HBM_GBS, 3),
                                           "inputs": "3 copies in rotation"}
         del gx
 

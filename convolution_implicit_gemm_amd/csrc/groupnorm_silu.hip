@@ -142,9 +142,21 @@ __global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(const _Float16 *_
         for (int u = 0; u < U; ++u) accumulate(h[u]);
         cnt += 8.0f * U;
     }
-    for (; v < v_end; v += vox_step) {
-        accumulate(xs[v * vpv + vi]);
-        cnt += 8.0f;
+    // the last (fewer than U) steps: their loads in flight together too,
+    // rather than one round trip each
+    if (v < v_end) {
+        half8_t h[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t vu = v + u * vox_step;
+            h[u] = vu < v_end ? xs[vu * vpv + vi] : half8_t{};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (v + u * vox_step < v_end) {
+                accumulate(h[u]);
+                cnt += 8.0f;
+            }
     }
     Welford w;
     w.n = cnt;
@@ -297,7 +309,18 @@ __global__ __launch_bounds__(kMaxThreads) void gn_apply_kernel(const _Float16 *_
             for (int u = 0; u < U; ++u) h[u] = hn[u];
         }
     }
-    for (; v < thw; v += vox_step) __builtin_nontemporal_store(apply(__builtin_nontemporal_load(xs + v * vpv + vi)), ys + v * vpv + vi);
+    // the last (fewer than U) steps, their loads in flight together
+    if (v < thw) {
+        half8_t h[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t vu = v + u * vox_step;
+            h[u] = vu < thw ? __builtin_nontemporal_load(xs + vu * vpv + vi) : half8_t{};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (v + u * vox_step < thw) __builtin_nontemporal_store(apply(h[u]), ys + (v + u * vox_step) * vpv + vi);
+    }
 }
 
 template <typename E>
