@@ -592,18 +592,40 @@ __global__ __launch_bounds__(kPsThreads) void conv3d_ps_kernel(ConvParams p) {
 // own XCD's range first (in walk order), then those of the other XCDs' ranges,
 // then the K-pieces.  p.queue holds 9 counters (one per range, one for the
 // K-pieces), zero at launch; a counter past its range's end means the range
-// is done.
-__device__ __forceinline__ int ps_grab(const ConvParams &p) {
+// is done.  `done` (thread 0's, across calls) marks the ranges this workgroup
+// has seen done.  Once its own range is done, one round trip reads all the
+// counters and the next goes to a range with tiles left, instead of trying
+// the ranges one atomic at a time.
+__device__ __forceinline__ int ps_grab(const ConvParams &p, uint32_t &done) {
     uint32_t xcc;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
     const int per = p.dp_tiles >> 3, rem = p.dp_tiles & 7;
-    for (int k = 0; k < 8; ++k) {
-        const int q = (int)((xcc + (uint32_t)k) & 7u);
-        const int len = per + (q < rem ? 1 : 0);
-        if (len == 0) continue;
-        const unsigned i = atomicAdd(p.queue + q, 1u);
-        if ((int)i < len) return q * per + (q < rem ? q : rem) + (int)i;
+    auto len_of = [&](int q) { return per + (q < rem ? 1 : 0); };
+    auto first_of = [&](int q) { return q * per + (q < rem ? q : rem); };
+    const int own = (int)xcc;
+    if (!(done & (1u << own)) && len_of(own) > 0) {
+        const unsigned i = atomicAdd(p.queue + own, 1u);
+        if ((int)i < len_of(own)) return first_of(own) + (int)i;
     }
+    done |= 1u << own;
+    // every failed take means a range was done in the meantime: at most 8 rounds
+    for (int round = 0; round < 8 && done != 0xFFu; ++round) {
+        unsigned c[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) c[q] = __hip_atomic_load(p.queue + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int pick = -1;
+#pragma unroll
+        for (int k = 1; k < 8; ++k) {
+            const int q = (own + k) & 7;
+            if ((int)c[q] >= len_of(q)) done |= 1u << q;
+            else if (pick < 0) pick = q;
+        }
+        if (pick < 0) break;
+        const unsigned i = atomicAdd(p.queue + pick, 1u);
+        if ((int)i < len_of(pick)) return first_of(pick) + (int)i;
+        done |= 1u << pick;
+    }
+    done = 0xFFu;
     const int pieces = p.sk_tiles * p.sk_pieces;
     if (pieces > 0) {
         const unsigned i = atomicAdd(p.queue + 8, 1u);
@@ -613,24 +635,42 @@ __device__ __forceinline__ int ps_grab(const ConvParams &p) {
 }
 
 template <bool TAIL, typename E>
-__global__ __launch_bounds__(kPsThreads) void conv3d_ps_dyn_kernel(ConvParams p) {
+__global__ __launch_bounds__(kPsThreads) void conv3d_ps_dyn_kernel(ConvParams p0) {
     __shared__ __attribute__((aligned(1024))) char smem[kPsLds + 256];
-    int *s_unit = reinterpret_cast<int *>(smem + kPsLds);
-    // thread 0 takes the next unit while the workgroup runs the current one
-    int next = 0;
-    if (threadIdx.x == 0) next = ps_grab(p);
-    for (;;) {
-        if (threadIdx.x == 0) *s_unit = next;
+    // Nothing is carried in vector registers from one unit to the next: the
+    // units go through LDS, slot k & 1 for the k-th (thread 0 writes unit k + 1
+    // while unit k runs, after every wave has read unit k - 1 from that slot),
+    // and thread 0's mask of done ranges sits in a third slot.  The parameters
+    // are read again from the kernel arguments for every unit (through a
+    // pointer the compiler cannot see through), so that they do not hold
+    // scalar registers across units either.
+    int *s_slot = reinterpret_cast<int *>(smem + kPsLds);
+    if (threadIdx.x == 0) {
+        uint32_t done = 0;
+        s_slot[0] = ps_grab(p0, done);
+        s_slot[2] = (int)done;
+    }
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint64_t kaddr = (uint64_t)__builtin_amdgcn_kernarg_segment_ptr();
+#endif
+    for (int k = 0;; ++k) {
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        const int u = __builtin_amdgcn_readfirstlane(*s_unit);
-        // every wave has read the unit before thread 0 may write the next one
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
+        const int u = __builtin_amdgcn_readfirstlane(s_slot[k & 1]);
         if (u < 0) break;
-        if (threadIdx.x == 0) next = ps_grab(p);
+#if defined(__HIP_DEVICE_COMPILE__)
+        uint64_t ka = kaddr;
+        asm volatile("" : "+s"(ka));
+        const ConvParams p = *reinterpret_cast<const ConvParams __attribute__((address_space(4))) *>(ka);
+#else
+        const ConvParams &p = p0;
+#endif
+        if (threadIdx.x == 0) {
+            uint32_t done = (uint32_t)s_slot[2];
+            s_slot[(k + 1) & 1] = ps_grab(p, done);
+            s_slot[2] = (int)done;
+        }
         int tile, it0, it1, slot;
         ps_unit_of(p, u, tile, it0, it1, slot);
         ps_unit<TAIL, E>(p, smem, tile, it0, it1, slot);
