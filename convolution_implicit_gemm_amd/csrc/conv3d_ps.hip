@@ -44,6 +44,11 @@
 //            slab and waited for before the barrier that starts the next.
 // K-pieces of a split tile start and end on slab boundaries.
 //
+// Epilogue.  A whole tile's accumulators start at its bias; at the end the
+// tile is rounded once (after adding the residual, if any) and staged in LDS,
+// which the K loop no longer needs, so that it leaves in whole rows rather
+// than as 16-byte pieces of 32 rows per instruction.
+//
 // Tile order.  Each XCD walks a contiguous range of tiles in blocks of 4 frames
 // x 8 tiles (ps_walk), so that the 32 tiles it runs at once share their input
 // rows in its L2; against tiles along one frame this cut the 33-frame 256x256
