@@ -125,9 +125,15 @@ typedef struct {
  * The plan may split the K range of the tiles that do not fill a whole wave
  * of workgroups into pieces that run concurrently and leave fp32 partial
  * tiles in the workspace, summed by a second small kernel; the workspace then
- * holds those partials.  The environment variable CONV3D_FORCE_PATH=general
- * behaves like CONV3D_F_NO_T1_FASTPATH; CONV3D_TILE=<name> forces a tile
- * configuration; CONV3D_STREAMK=0 forbids and =1 forces the K split.
+ * holds those partials.  For long grids (at least 8 waves of whole tiles) of
+ * the row-slab tile, the plan launches one workgroup per CU that takes tiles
+ * from counters at the end of the workspace (64 bytes, cleared by a small
+ * kernel at the start of each call), so that the XCDs, which clock
+ * differently, finish together.  The environment variable
+ * CONV3D_FORCE_PATH=general behaves like CONV3D_F_NO_T1_FASTPATH;
+ * CONV3D_TILE=<name> forces a tile configuration; CONV3D_STREAMK=0 forbids and
+ * =1 forces the K split; CONV3D_DYNAMIC=0 forbids and =1 forces the
+ * one-workgroup-per-CU schedule where the row-slab tile is used.
  */
 conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *workspace_bytes);
 
@@ -142,8 +148,8 @@ void conv3d_plan_destroy(conv3d_plan_t p);
  * x, weight, y: required device pointers.  bias / residual: required when the
  * plan's flags say so, otherwise ignored.  workspace: device memory of at
  * least the planned size (may be NULL when that size is 0): folded first-frame
- * weights and/or fp32 partial tiles; its contents are scratch, overwritten by
- * each call.  Calls on different streams must not
+ * weights, fp32 partial tiles and/or tile counters; its contents are scratch,
+ * overwritten by each call.  Calls on different streams must not
  * share a workspace.  y must not overlap x, weight, bias or residual.
  * Errors: INVALID_ARG (null/misaligned pointers, y aliasing an input),
  * WORKSPACE (workspace_bytes below the planned size), HIP (launch failure).
