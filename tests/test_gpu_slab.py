@@ -158,6 +158,27 @@ def test_slab_kernel_dynamic_schedule_bias_residual_equals_static():
     assert_conv_close(y1, ref, mag, "slab kernel, dynamic schedule, bias + residual")
 
 
+RES_EDGE_CASES = [
+    ConvShape(1, 3, 3, 32, 64, 96, pad_t_front=2, tmode=Z),   # M = 288: a last tile of 32 voxels; Cout < 256
+    ConvShape(1, 2, 4, 96, 40, 264),                          # tiles inside rows, channel tail, a column tile of 8
+]
+
+
+@pytest.mark.parametrize("case", range(len(RES_EDGE_CASES)))
+def test_slab_kernel_residual_edges_exact(case):
+    # the epilogue staged through LDS with a residual: rows past the output and
+    # channels past Cout are never read or written; ternary data, bit-exact
+    s = RES_EDGE_CASES[case]
+    x, w = ternary(s.x_shape, 480 + case), ternary(s.w_shape, 482 + case)
+    b = np.random.default_rng(484 + case).integers(-2, 3, s.cout).astype(np.float16)
+    res = np.random.default_rng(486 + case).integers(-3, 4, out_dims(s)).astype(np.float16)
+    y, info = run_conv(s, x, w, b, res=res, tile=TILE, split="0")
+    assert info.kernel_name.decode().startswith("conv3d_igemm_" + TILE)
+    ref, _ = oracle_full(s, x, w, b, res)
+    assert np.array_equal(y.astype(np.float64), ref), "%d of %d outputs differ" % (
+        int((y.astype(np.float64) != ref).sum()), y.size)
+
+
 def test_slab_kernel_random_with_bias_and_residual_within_bound():
     s = ConvShape(1, 5, 16, 128, 256, 256)
     d = workloads.conv_inputs(s, 370)
