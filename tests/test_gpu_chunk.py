@@ -75,6 +75,32 @@ def test_chunk_matches_conv_of_the_concatenation(case, strategy):
 
 
 @pytest.mark.parametrize("strategy", STRATEGIES)
+def test_chunked_decode_on_the_dynamic_tile_schedule(strategy):
+    # every plan forced onto the row-slab tile and the one-workgroup-per-CU
+    # schedule, whose tile counters then sit in each sub-plan's share of the
+    # chunk plan's workspace; ternary data, so chunked equals whole bit for bit
+    tc = 4
+    whole = ConvShape(1, 3 * tc, 8, 64, 64, 64, tmode=R)
+    rng = np.random.default_rng(990)
+    x = rng.integers(-1, 2, size=whole.x_shape).astype(np.float16)
+    w = rng.integers(-1, 2, size=whole.w_shape).astype(np.float16)
+    b = rng.integers(-2, 3, whole.cout).astype(np.float16)
+    part = ConvShape(1, tc, 8, 64, 64, 64, tmode=R)
+    with env_var("CONV3D_TILE", "m256n256k64ps"), env_var("CONV3D_DYNAMIC", "1"):
+        y_whole, info = run_conv(whole, x, w, b)
+        assert info.grid <= 256
+        y0, _ = run_conv(part, x[:, :tc], w, b)
+        parts = [y0]
+        for k in (1, 2):
+            hist = [k * tc - 2, k * tc - 1]
+            parts.append(chunk(part, np.ascontiguousarray(x[:, hist]), x[:, k * tc:(k + 1) * tc], w, b,
+                               strategy=strategy))
+    assert np.array_equal(np.concatenate(parts, axis=1), y_whole)
+    ref, _ = oracle.conv3d(widen(x), widen(w), widen(b), None, whole.pads, whole.tmode)
+    assert np.array_equal(widen(y_whole), ref)
+
+
+@pytest.mark.parametrize("strategy", STRATEGIES)
 @pytest.mark.parametrize("n,tc", [(1, 6), (2, 3), (1, 1)])
 def test_chunked_decode_equals_whole_video_decode(n, tc, strategy):
     # a video of 3 chunks of tc frames: chunk 0 with the causal (replicate)
