@@ -13,17 +13,25 @@
 //          pass),
 //          then the block merges threads of a group (Chan's pairwise
 //          update) and writes (count, mean, M2) partials.
-//  final:  grid (G, N), one block per (sample, group): every thread loads its
-//          share of the group's SB partials (one contiguous run), merges them, and the block
-//          reduces (shuffles, then LDS) to the group's mean and rstd; it
-//          writes per-channel scale a = gamma*rstd and shift b = beta - mean*a.
-//  apply:  grid (AB, N).  Each thread owns one channel vector, keeps its 8
-//          scales/shifts in registers, and streams y = x*a + b, then
-//          y*sigmoid(y), rounded once to fp16, with the next batch of loads
-//          in flight while a batch is converted.
+//  apply:  grid (MB, N) of persistent blocks (128 over all samples).  Every
+//          block first merges each group's SB partials (one contiguous run
+//          per group, a power-of-two team of threads per group, then
+//          xor-shuffles) to the group's mean and rstd, while its first batch
+//          of x loads is in flight.  Each thread owns one channel vector,
+//          derives its 8 scales a = gamma*rstd and shifts b = beta - mean*a,
+//          and streams y = x*a + b, then y*sigmoid(y), rounded once to fp16,
+//          with the next batch of loads in flight while a batch is converted.
+//          Every block merges in the same order, so all of them use the same
+//          scales and shifts.
+//  final + plain apply: where the partials of all groups exceed 256 KiB (many
+//          groups), a final kernel, grid (G, N), merges each group once and
+//          writes the per-channel scales and shifts to the workspace, and
+//          2048 apply blocks read them.  CONV3D_GN_FINAL=1 takes this path
+//          for every shape (a measurement switch).
 #include "c3d_internal.h"
 #include "elem16.h"
 
+#include <cstdlib>
 #include <mutex>
 
 // Scratch of groupnorm_silu_noalloc, for callers that cannot allocate device
@@ -47,7 +55,15 @@ struct GnGeom {
     int athreads;   // apply block size: a multiple of vpv
     int sb;         // stats blocks per sample
     int ab;         // apply blocks per sample
+    // merged apply (the per-group merge in every apply block, no final kernel)
+    bool merged;
+    int mthreads;   // its block size: the largest multiple of vpv up to 1024
+    int mb;         // its blocks per sample (about one per CU over all samples)
+    int tpg;        // threads merging one group: a power of two up to 64
 };
+
+// Largest merge a merged apply block does: groups x sb partials of 16 bytes.
+constexpr size_t kMaxMergeBytes = (size_t)256 << 10;
 
 // Smallest multiple of vpv that is at least `least` threads (and a multiple of
 // 64 where that fits in a block).
@@ -59,15 +75,17 @@ int gn_block(int vpv, int least) {
     return (t64 % 64 == 0) ? t64 : t;
 }
 
-GnGeom gn_geom(int32_t n, int64_t thw, int32_t c) {
+GnGeom gn_geom(int32_t n, int64_t thw, int32_t c, int32_t groups) {
     GnGeom g;
     g.vpv = c / 8;
-    // stats: about 512 large blocks over the whole tensor (fewer partials for
-    // the merge), each at least 4 passes deep; apply: about 2048 blocks
+    // stats: about 256 large blocks over the whole tensor (one per CU; fewer
+    // partials for the merge), each at least 4 passes deep; plain apply:
+    // about 2048 blocks; merged apply: about 128 blocks of up to 1024
+    // threads, so that the partials are read by few blocks
     g.sthreads = gn_block(g.vpv, 512);
     g.athreads = gn_block(g.vpv, 256);
     const int svox = g.sthreads / g.vpv, avox = g.athreads / g.vpv;
-    int64_t want = (512 + n - 1) / n;
+    int64_t want = (256 + n - 1) / n;
     int64_t maxb = (thw + 4 * svox - 1) / (4 * svox);
     g.sb = (int)(want < maxb ? want : maxb);
     if (g.sb < 1) g.sb = 1;
@@ -75,6 +93,19 @@ GnGeom gn_geom(int32_t n, int64_t thw, int32_t c) {
     int64_t maxa = (thw + 4 * avox - 1) / (4 * avox);
     g.ab = (int)(wanta < maxa ? wanta : maxa);
     if (g.ab < 1) g.ab = 1;
+    g.mthreads = (kMaxThreads / g.vpv) * g.vpv;
+    g.tpg = 0;
+    if (g.mthreads > 0 && groups <= g.mthreads) {
+        const int most = g.mthreads / groups < 64 ? g.mthreads / groups : 64;
+        g.tpg = 1;
+        while (g.tpg * 2 <= most) g.tpg *= 2;
+    }
+    const int mvox = g.mthreads > 0 ? g.mthreads / g.vpv : 1;
+    int64_t wantm = (128 + n - 1) / n;
+    int64_t maxm = (thw + 4 * mvox - 1) / (4 * mvox);
+    g.mb = (int)(wantm < maxm ? wantm : maxm);
+    if (g.mb < 1) g.mb = 1;
+    g.merged = g.tpg > 0 && (size_t)groups * g.sb * sizeof(float4) <= kMaxMergeBytes;
     return g;
 }
 
@@ -257,42 +288,29 @@ __device__ __forceinline__ float silu_f32(float y) {
     return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Streams y = silu(x*a + b) over voxels v, v + vox_step, ... of one sample,
+// four 16-byte loads per batch with the next batch in flight while one is
+// converted and stored.  h holds the batch at v already when `loaded`.
 template <bool SILU, typename E>
-__global__ __launch_bounds__(kMaxThreads) void gn_apply_kernel(const _Float16 *__restrict__ x,
-                                                              _Float16 *__restrict__ y, int64_t thw,
-                                                              int32_t c, const float *__restrict__ scale,
-                                                              const float *__restrict__ shift) {
-    const int n = blockIdx.y;
-    const int vpv = c / 8;
-    const int tid = threadIdx.x;
-    const int vi = tid % vpv;
-    const int vox_step = (blockDim.x / vpv) * gridDim.x;
-    float a[8], bsh[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        a[q] = scale[(size_t)n * c + vi * 8 + q];
-        bsh[q] = shift[(size_t)n * c + vi * 8 + q];
-    }
-    const half8_t *xs = reinterpret_cast<const half8_t *>(x + (size_t)n * thw * c);
-    half8_t *ys = reinterpret_cast<half8_t *>(y + (size_t)n * thw * c);
-    int64_t v = (int64_t)blockIdx.x * (blockDim.x / vpv) + tid / vpv;
-    auto apply = [&](const half8_t h) {
+__device__ __forceinline__ void apply_stream(const half8_t *__restrict__ xs, half8_t *__restrict__ ys, int64_t thw,
+                                             int vpv, int vi, int64_t v, int64_t vox_step, const float (&a)[8],
+                                             const float (&bsh)[8], half8_t (&h)[4], bool loaded) {
+    auto apply = [&](const half8_t hv) {
         half8_t o;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            float t = fmaf(to_f32<E>(h[q]), a[q], bsh[q]);
+            float t = fmaf(to_f32<E>(hv[q]), a[q], bsh[q]);
             if (SILU) t = silu_f32(t);
             o[q] = from_f32<E>(t);
         }
         return o;
     };
-    // four 16-byte loads per batch; the next batch is in flight while this
-    // one is converted and stored
     constexpr int U = 4;
-    half8_t h[U];
     if (v + (U - 1) * vox_step < thw) {
+        if (!loaded) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) h[u] = __builtin_nontemporal_load(xs + (v + u * vox_step) * vpv + vi);
+            for (int u = 0; u < U; ++u) h[u] = __builtin_nontemporal_load(xs + (v + u * vox_step) * vpv + vi);
+        }
         for (;;) {
             const int64_t vn = v + U * vox_step;
             const bool more = vn + (U - 1) * vox_step < thw;
@@ -311,22 +329,111 @@ __global__ __launch_bounds__(kMaxThreads) void gn_apply_kernel(const _Float16 *_
     }
     // the last (fewer than U) steps, their loads in flight together
     if (v < thw) {
-        half8_t h[U];
+        half8_t t[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t vu = v + u * vox_step;
-            h[u] = vu < thw ? __builtin_nontemporal_load(xs + vu * vpv + vi) : half8_t{};
+            t[u] = vu < thw ? __builtin_nontemporal_load(xs + vu * vpv + vi) : half8_t{};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (v + u * vox_step < thw) __builtin_nontemporal_store(apply(h[u]), ys + (v + u * vox_step) * vpv + vi);
+            if (v + u * vox_step < thw) __builtin_nontemporal_store(apply(t[u]), ys + (v + u * vox_step) * vpv + vi);
     }
+}
+
+template <bool SILU, typename E>
+__global__ __launch_bounds__(kMaxThreads) void gn_apply_kernel(const _Float16 *__restrict__ x,
+                                                              _Float16 *__restrict__ y, int64_t thw,
+                                                              int32_t c, const float *__restrict__ scale,
+                                                              const float *__restrict__ shift) {
+    const int n = blockIdx.y;
+    const int vpv = c / 8;
+    const int tid = threadIdx.x;
+    const int vi = tid % vpv;
+    const int64_t vox_step = (int64_t)(blockDim.x / vpv) * gridDim.x;
+    float a[8], bsh[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        a[q] = scale[(size_t)n * c + vi * 8 + q];
+        bsh[q] = shift[(size_t)n * c + vi * 8 + q];
+    }
+    const half8_t *xs = reinterpret_cast<const half8_t *>(x + (size_t)n * thw * c);
+    half8_t *ys = reinterpret_cast<half8_t *>(y + (size_t)n * thw * c);
+    const int64_t v = (int64_t)blockIdx.x * (blockDim.x / vpv) + tid / vpv;
+    half8_t h[4];
+    apply_stream<SILU, E>(xs, ys, thw, vpv, vi, v, vox_step, a, bsh, h, false);
+}
+
+// The apply pass with the per-group merge done in every block instead of in a
+// separate final kernel: persistent blocks (about one per CU), each merging
+// all `groups` groups' sb partials of its sample (tpg threads per group, a
+// power of two up to 64, then xor-shuffles within the tpg lanes) while its
+// first batch of x loads is in flight.  Every block merges in the same order,
+// so all blocks derive the same scale and shift.
+template <bool SILU, typename E>
+__global__ __launch_bounds__(kMaxThreads) void gn_apply_merge_kernel(
+    const _Float16 *__restrict__ x, _Float16 *__restrict__ y, int64_t thw, int32_t c, int32_t groups, int32_t sb,
+    int32_t tpg, const float4 *__restrict__ part, float eps, const _Float16 *__restrict__ gamma,
+    const _Float16 *__restrict__ beta) {
+    __shared__ float2 stat[kMaxThreads];
+    const int n = blockIdx.y;
+    const int vpv = c / 8;
+    const int tid = threadIdx.x;
+    const int vi = tid % vpv;
+    const int64_t vox_step = (int64_t)(blockDim.x / vpv) * gridDim.x;
+    const half8_t *xs = reinterpret_cast<const half8_t *>(x + (size_t)n * thw * c);
+    half8_t *ys = reinterpret_cast<half8_t *>(y + (size_t)n * thw * c);
+    const int64_t v = (int64_t)blockIdx.x * (blockDim.x / vpv) + tid / vpv;
+    constexpr int U = 4;
+    half8_t h[U];
+    const bool loaded = v + (U - 1) * vox_step < thw;
+    if (loaded) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) h[u] = __builtin_nontemporal_load(xs + (v + u * vox_step) * vpv + vi);
+    }
+    // merge: group g by threads g*tpg ... g*tpg + tpg-1
+    const int g = tid / tpg, j = tid % tpg;
+    Welford acc = {0.0f, 0.0f, 0.0f};
+    if (g < groups) {
+        const float4 *p = part + ((size_t)n * groups + g) * sb;
+        int b = j;
+        for (; b + 7 * tpg < sb; b += 8 * tpg) {
+            float4 e[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) e[u] = p[b + u * tpg];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc = chan_merge(acc, Welford{e[u].x, e[u].y, e[u].z});
+        }
+        for (; b < sb; b += tpg) {
+            const float4 e = p[b];
+            acc = chan_merge(acc, Welford{e.x, e.y, e.z});
+        }
+    }
+    for (int off = tpg >> 1; off > 0; off >>= 1) {
+        Welford o;
+        o.n = __shfl_xor(acc.n, off);
+        o.mean = __shfl_xor(acc.mean, off);
+        o.m2 = __shfl_xor(acc.m2, off);
+        acc = chan_merge(acc, o);
+    }
+    if (g < groups && j == 0) stat[g] = make_float2(acc.mean, 1.0f / sqrtf(acc.m2 / acc.n + eps));
+    __syncthreads();
+    const int cg = c / groups;
+    float a[8], bsh[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int ch = vi * 8 + q;
+        const float2 st = stat[ch / cg];
+        a[q] = st.y * to_f32<E>(gamma[ch]);
+        bsh[q] = to_f32<E>(beta[ch]) - st.x * a[q];
+    }
+    apply_stream<SILU, E>(xs, ys, thw, vpv, vi, v, vox_step, a, bsh, h, loaded);
 }
 
 template <typename E>
 hipError_t launch_gn(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta, _Float16 *y, int32_t n,
                      int64_t thw, int32_t c, int32_t groups, float eps, int32_t silu, void *ws, hipStream_t s) {
-    const GnGeom g = gn_geom(n, thw, c);
+    const GnGeom g = gn_geom(n, thw, c, groups);
     char *base = static_cast<char *>(ws);
     float *scale = reinterpret_cast<float *>(base);
     float *shift = scale + (size_t)n * c;
@@ -334,6 +441,17 @@ hipError_t launch_gn(const _Float16 *x, const _Float16 *gamma, const _Float16 *b
     hipLaunchKernelGGL(gn_stats_kernel<E>, dim3(g.sb, n), dim3(g.sthreads), 0, s, x, thw, c, groups, g.sb, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // CONV3D_GN_FINAL=1 keeps the separate final kernel (for measurements)
+    const char *fin = getenv("CONV3D_GN_FINAL");
+    if (g.merged && !(fin && *fin == '1')) {
+        if (silu)
+            hipLaunchKernelGGL((gn_apply_merge_kernel<true, E>), dim3(g.mb, n), dim3(g.mthreads), 0, s, x, y, thw, c,
+                               groups, g.sb, g.tpg, part, eps, gamma, beta);
+        else
+            hipLaunchKernelGGL((gn_apply_merge_kernel<false, E>), dim3(g.mb, n), dim3(g.mthreads), 0, s, x, y, thw,
+                               c, groups, g.sb, g.tpg, part, eps, gamma, beta);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(gn_final_kernel<E>, dim3(groups, n), dim3(kFinalThreads), 0, s, part, g.sb, c, groups, eps,
                        gamma, beta, scale, shift);
     e = hipGetLastError();
@@ -371,7 +489,7 @@ hipError_t gn_static_scratch(void **ptr) {
 }
 
 size_t gn_workspace_bytes(int32_t n, int64_t thw, int32_t c, int32_t groups) {
-    const GnGeom g = gn_geom(n, thw, c);
+    const GnGeom g = gn_geom(n, thw, c, groups);
     return off_part(n, c) + (size_t)n * g.sb * groups * sizeof(float4);
 }
 

@@ -196,7 +196,11 @@ conv3d_status conv3d_forward_chunk(conv3d_plan_t p, const void *x_prev, const vo
  * statistics and per-channel scale/shift); its contents are scratch,
  * overwritten by each call, so calls that may run concurrently must not
  * share one.  groupnorm_silu_workspace() returns 0 for arguments that
- * groupnorm_silu would reject.
+ * groupnorm_silu would reject.  Two launches: a statistics pass, then an
+ * apply pass whose blocks first merge the partial statistics themselves
+ * (three launches, with a separate merge, when one sample's partials exceed
+ * 256 KiB; the environment variable CONV3D_GN_FINAL=1 forces that path, for
+ * measurements).
  * Errors: INVALID_ARG (null/misaligned pointers, non-positive sizes,
  * c % groups != 0, eps < 0), UNSUPPORTED ((c/groups) % 8 != 0, or c > 8192),
  * WORKSPACE, HIP.

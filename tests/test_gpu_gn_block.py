@@ -51,12 +51,19 @@ GN_CASES = [  # (n, thw_shape, c, groups, mean, std)
     (1, (3, 3, 3), 8, 1, 0.0, 1.0),           # the fewest channels: 8 in one group
     (1, (1, 13, 17), 96, 12, -2.0, 0.5),      # odd voxel count, 8-channel groups
     (1, (1, 2, 3), 8192, 32, 0.0, 1.0),       # the most channels
+    (1, (4, 32, 32), 1024, 128, 0.0, 1.0),    # 128 groups: partials beyond one apply block's merge
+    (2, (4, 16, 16), 2048, 256, 1.0, 3.0),    # 256 groups of 8 channels, two samples
 ]
 
 
 @pytest.mark.parametrize("case", range(len(GN_CASES)))
 @pytest.mark.parametrize("silu", [True, False])
-def test_groupnorm_silu_small(case, silu):
+@pytest.mark.parametrize("final_kernel", [False, True])
+def test_groupnorm_silu_small(case, silu, final_kernel, monkeypatch):
+    # final_kernel: CONV3D_GN_FINAL=1 takes the separate final kernel and the
+    # plain apply for every shape; otherwise the apply blocks merge the
+    # partials themselves wherever they fit (256 KiB), as the library chooses
+    monkeypatch.setenv("CONV3D_GN_FINAL", "1" if final_kernel else "0")
     n, thw, c, g, mean, std = GN_CASES[case]
     d = workloads.gn_inputs(n, thw, c, 800 + case, mean, std)
     y = gn_gpu(d["x"], d["gamma"], d["beta"], g, silu=silu).cpu().numpy()
@@ -85,7 +92,9 @@ def test_in_place_and_workspace_reuse():
         assert_gn_close(y, ref, "rep %d" % rep)
 
 
-def test_decoder_block_groupnorm_full_size():
+@pytest.mark.parametrize("final_kernel", [False, True])
+def test_decoder_block_groupnorm_full_size(final_kernel, monkeypatch):
+    monkeypatch.setenv("CONV3D_GN_FINAL", "1" if final_kernel else "0")
     d = workloads.workload_inputs(4)
     y = gn_gpu(d["x"], d["gamma1"], d["beta1"], 32).cpu().numpy()
     ref = oracle.groupnorm_silu(d["x"], d["gamma1"], d["beta1"], 32, 1e-6, True)
