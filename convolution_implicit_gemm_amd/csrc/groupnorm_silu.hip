@@ -13,7 +13,7 @@
 //          pass),
 //          then the block merges threads of a group (Chan's pairwise
 //          update) and writes (count, mean, M2) partials.
-//  apply:  grid (MB, N) of persistent blocks (128 over all samples).  Every
+//  apply:  grid (MB, N) of persistent blocks (256 over all samples).  Every
 //          block first merges each group's SB partials (one contiguous run
 //          per group, a power-of-two team of threads per group, then
 //          xor-shuffles) to the group's mean and rstd, while its first batch
@@ -80,8 +80,8 @@ GnGeom gn_geom(int32_t n, int64_t thw, int32_t c, int32_t groups) {
     g.vpv = c / 8;
     // stats: about 256 large blocks over the whole tensor (one per CU; fewer
     // partials for the merge), each at least 4 passes deep; plain apply:
-    // about 2048 blocks; merged apply: about 128 blocks of up to 1024
-    // threads, so that the partials are read by few blocks
+    // about 2048 blocks; merged apply: about 256 blocks of about 512 threads
+    // (the channel vectors of one voxel when they exceed 512)
     g.sthreads = gn_block(g.vpv, 512);
     g.athreads = gn_block(g.vpv, 256);
     const int svox = g.sthreads / g.vpv, avox = g.athreads / g.vpv;
@@ -93,7 +93,7 @@ GnGeom gn_geom(int32_t n, int64_t thw, int32_t c, int32_t groups) {
     int64_t maxa = (thw + 4 * avox - 1) / (4 * avox);
     g.ab = (int)(wanta < maxa ? wanta : maxa);
     if (g.ab < 1) g.ab = 1;
-    g.mthreads = (kMaxThreads / g.vpv) * g.vpv;
+    g.mthreads = g.vpv <= 512 ? (512 / g.vpv) * g.vpv : g.vpv;
     g.tpg = 0;
     if (g.mthreads > 0 && groups <= g.mthreads) {
         const int most = g.mthreads / groups < 64 ? g.mthreads / groups : 64;
@@ -101,7 +101,7 @@ GnGeom gn_geom(int32_t n, int64_t thw, int32_t c, int32_t groups) {
         while (g.tpg * 2 <= most) g.tpg *= 2;
     }
     const int mvox = g.mthreads > 0 ? g.mthreads / g.vpv : 1;
-    int64_t wantm = (128 + n - 1) / n;
+    int64_t wantm = (256 + n - 1) / n;
     int64_t maxm = (thw + 4 * mvox - 1) / (4 * mvox);
     g.mb = (int)(wantm < maxm ? wantm : maxm);
     if (g.mb < 1) g.mb = 1;
