@@ -440,6 +440,25 @@ def main():
         result["decoder_block_config"] = ("GN(32, eps 1e-6)+SiLU -> causal conv3d 3x3x3 -> GN+SiLU -> "
                                           "causal conv3d 3x3x3 -> +x; N=1 C=256 T=17 H=W=128 fp16")
 
+    if "block" in extras or args.no_kernels:
+        # the same block with GN2's statistics taken in conv1's epilogue
+        # (CONV3D_F_GN_STATS) and GN2 normalising from them
+        bp1s = c3d.conv3d_plan(desc_of(c3d, s4, c3d.CONV3D_F_BIAS | c3d.CONV3D_F_GN_STATS))
+        bws1s = ws_for(bp1s, torch, dev)
+        sst, sslots = c3d.gn_stats_view(bp1s, bws1s)
+        sws = torch.empty(c3d.groupnorm_silu_from_stats_workspace(1, s4.cout, 32), dtype=torch.uint8, device=dev)
+
+        def block_stats():
+            c3d.groupnorm_silu(bx, bt["gamma1"], bt["beta1"], a1, 1, thw, s4.cin, 32, 1e-6, True, gws)
+            c3d.conv3d_forward(bp1s, a1, bt["w1"], bt["b1"], None, c1, bws1s)
+            c3d.groupnorm_silu_from_stats(c1, bt["gamma2"], bt["beta2"], a2, 1, thw, s4.cout, 32, 1e-6, True,
+                                          sst, sslots, sws)
+            c3d.conv3d_forward(bp2, a2, bt["w2"], bt["b2"], bx, out, bws2)
+
+        log("decoder block, GN2 from conv1's statistics")
+        _, bper, _ = time_steps(block_stats, 20, 5, torch, args.warm_seconds)
+        result["decoder_block_gn2_from_conv1_stats_ms"] = round(sum(bper) / len(bper), 4)
+
     if not args.no_kernels and "conv256" in extras:
         conv_extra("causal_conv_256_T17_128x128", bp1,
                    lambda: c3d.conv3d_forward(bp1, a1, bt["w1"], bt["b1"], None, c1, bws1), steps=40, warmup=20)

@@ -30,6 +30,7 @@ CONV3D_F_RESIDUAL = 2
 CONV3D_F_NO_T1_FASTPATH = 4
 CONV3D_F_BF16 = 8
 CONV3D_F_CHUNK = 16
+CONV3D_F_GN_STATS = 32
 
 CONV3D_PATH_GENERAL = 0
 CONV3D_PATH_T1_FOLD = 1
@@ -38,6 +39,7 @@ CONV3D_PATH_POINTWISE = 2
 EXPORTED = ("conv3d_plan", "conv3d_plan_query", "conv3d_plan_destroy", "conv3d_forward",
             "conv3d_forward_chunk",
             "groupnorm_silu_workspace", "groupnorm_silu", "groupnorm_silu_bf16",
+            "groupnorm_silu_from_stats_workspace", "groupnorm_silu_from_stats", "groupnorm_silu_from_stats_bf16",
             "groupnorm_silu_noalloc_max_bytes", "groupnorm_silu_noalloc",
             "conv3d_calibrate_scratch_bytes",
             "conv3d_calibrate_mfma", "conv3d_calibrate_hbm", "conv3d_clock_stamp_bytes",
@@ -59,7 +61,8 @@ class conv3d_plan_info(ctypes.Structure):
                 ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32), ("stages", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("grid", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_size_t), ("kernel_name", ctypes.c_char * 64),
-                ("split_tiles", ctypes.c_int32), ("split_pieces", ctypes.c_int32)]
+                ("split_tiles", ctypes.c_int32), ("split_pieces", ctypes.c_int32),
+                ("gn_stats_slots", ctypes.c_int32), ("gn_stats_offset", ctypes.c_size_t)]
 
 
 class Conv3dError(RuntimeError):
@@ -102,6 +105,13 @@ def load_library(path: str = LIB_PATH):
     lib.groupnorm_silu_bf16.argtypes = lib.groupnorm_silu.argtypes
     lib.groupnorm_silu_bf16.restype = ctypes.c_int
     lib.groupnorm_silu.restype = ctypes.c_int
+    lib.groupnorm_silu_from_stats_workspace.argtypes = [i32, i32, i32]
+    lib.groupnorm_silu_from_stats_workspace.restype = sz
+    lib.groupnorm_silu_from_stats.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_float, i32, vp, i32,
+                                              vp, sz, vp]
+    lib.groupnorm_silu_from_stats.restype = ctypes.c_int
+    lib.groupnorm_silu_from_stats_bf16.argtypes = lib.groupnorm_silu_from_stats.argtypes
+    lib.groupnorm_silu_from_stats_bf16.restype = ctypes.c_int
     lib.groupnorm_silu_noalloc_max_bytes.argtypes = []
     lib.groupnorm_silu_noalloc_max_bytes.restype = sz
     lib.groupnorm_silu_noalloc.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_float, i32, vp]
@@ -278,6 +288,35 @@ def groupnorm_silu(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, worksp
     _check(fn(_addr(x, "x", ne, dt), _addr(gamma, "gamma", c, dt), _addr(beta, "beta", c, dt), _addr(y, "y", ne, dt),
               n, thw, c, groups, float(eps), 1 if apply_silu else 0, _addr(workspace, "workspace"),
               workspace_bytes, _stream(stream)))
+
+
+def groupnorm_silu_from_stats_workspace(n, c, groups) -> int:
+    return load_library().groupnorm_silu_from_stats_workspace(n, c, groups)
+
+
+def gn_stats_view(plan: Plan, workspace):
+    """(address, slots) of the GroupNorm partials a CONV3D_F_GN_STATS plan's
+    forward leaves in ``workspace`` (a device tensor of the planned size)."""
+    info = conv3d_plan_query(plan)
+    if not info.gn_stats_slots:
+        raise Conv3dError(CONV3D_ERR_INVALID_ARG, "the plan was made without CONV3D_F_GN_STATS")
+    if workspace.numel() * workspace.element_size() < plan.workspace_bytes:
+        raise Conv3dError(CONV3D_ERR_WORKSPACE, "workspace smaller than the plan's")
+    return workspace.data_ptr() + info.gn_stats_offset, info.gn_stats_slots
+
+
+def groupnorm_silu_from_stats(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, stats, stats_slots,
+                              workspace, workspace_bytes=None, stream=None, bf16=False) -> None:
+    """Enqueue y = [SiLU](GroupNorm(x)) with x's statistics merged from the partials
+    ``stats`` (an address, see gn_stats_view) that the conv producing x wrote."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    lib = load_library()
+    fn = lib.groupnorm_silu_from_stats_bf16 if bf16 else lib.groupnorm_silu_from_stats
+    dt, ne = _elem_dtype(bf16), n * thw * c
+    _check(fn(_addr(x, "x", ne, dt), _addr(gamma, "gamma", c, dt), _addr(beta, "beta", c, dt), _addr(y, "y", ne, dt),
+              n, thw, c, groups, float(eps), 1 if apply_silu else 0, _addr(stats, "stats"), int(stats_slots),
+              _addr(workspace, "workspace"), workspace_bytes, _stream(stream)))
 
 
 def groupnorm_silu_noalloc_max_bytes() -> int:

@@ -153,6 +153,7 @@ struct conv3d_plan_s {
     size_t ws_fold;       // bytes of folded weights at the start of the workspace
     size_t ws_queue = 0;  // dynamic tile schedule: offset of its counters in the workspace
     bool dynamic = false;
+    size_t ws_gn = 0;     // CONV3D_F_GN_STATS: offset of the GroupNorm partials in the workspace
     size_t ws_bytes;
     int64_t x_elems, w_elems, y_elems;
     double flops;
@@ -208,9 +209,11 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
         return fail(CONV3D_ERR_INVALID_ARG, "padding must be smaller than the kernel extent");
     if (d->t_pad_mode != CONV3D_TPAD_ZERO && d->t_pad_mode != CONV3D_TPAD_REPLICATE)
         return fail(CONV3D_ERR_INVALID_ARG, "unknown t_pad_mode %d", d->t_pad_mode);
-    const uint32_t known =
-        CONV3D_F_BIAS | CONV3D_F_RESIDUAL | CONV3D_F_NO_T1_FASTPATH | CONV3D_F_BF16 | CONV3D_F_CHUNK;
+    const uint32_t known = CONV3D_F_BIAS | CONV3D_F_RESIDUAL | CONV3D_F_NO_T1_FASTPATH | CONV3D_F_BF16 |
+                           CONV3D_F_CHUNK | CONV3D_F_GN_STATS;
     if (d->flags & ~known) return fail(CONV3D_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags & ~known);
+    if ((d->flags & CONV3D_F_CHUNK) && (d->flags & CONV3D_F_GN_STATS))
+        return fail(CONV3D_ERR_INVALID_ARG, "CONV3D_F_GN_STATS cannot be combined with CONV3D_F_CHUNK");
     if (d->flags & CONV3D_F_CHUNK) return plan_chunk(d, out, workspace_bytes);
     const int To = d->t + d->pad_t_front + d->pad_t_back - d->kt + 1;
     const int Ho = d->h + 2 * d->pad_h - d->kh + 1;
@@ -252,6 +255,16 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
         path = CONV3D_PATH_POINTWISE;
     }
     p->path = path;
+    const bool gn_stats = (d->flags & CONV3D_F_GN_STATS) != 0;
+    if (gn_stats && path != CONV3D_PATH_GENERAL) {
+        delete p;
+        return fail(CONV3D_ERR_UNSUPPORTED, "CONV3D_F_GN_STATS needs the general path (not the %s)",
+                    path == CONV3D_PATH_T1_FOLD ? "T=1 fold: add CONV3D_F_NO_T1_FASTPATH" : "1x1x1 stream");
+    }
+    if (gn_stats && ((int64_t)To * Ho * Wo) % c3d::kPsBM) {
+        delete p;
+        return fail(CONV3D_ERR_UNSUPPORTED, "CONV3D_F_GN_STATS needs t_out*h_out*w_out a multiple of %d", c3d::kPsBM);
+    }
 
     c3d::ConvParams &q = p->prm;
     q.T = path == CONV3D_PATH_T1_FOLD ? 1 : d->t;
@@ -286,6 +299,7 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
         const c3d::TileCfg &t = tiles[i];
         if (forced && *forced && strcmp(forced, t.name) != 0) continue;
         if (t.supported && !t.supported(q)) continue;
+        if (gn_stats && !t.dynamic) continue;  // only the row-slab tile's epilogue writes the statistics
         const int64_t mt = (q.M + t.bm - 1) / t.bm, nt = (q.Cout + t.bn - 1) / t.bn;
         const int cpt = (q.Cin + t.bk - 1) / t.bk;
         const Decomp dcmp = decompose(t, mt * nt, q.kt * q.kh * q.kw * cpt, skmode);
@@ -293,6 +307,12 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
             best = &t;
             best_d = dcmp;
         }
+    }
+    if (!best && gn_stats) {
+        delete p;
+        return fail(CONV3D_ERR_UNSUPPORTED,
+                    "CONV3D_F_GN_STATS needs the row-slab tile (kw = 3, pad_w = 1, kt and kh <= 3, rows a multiple of "
+                    "32 voxels, w_out = w)%s", forced && *forced ? " and no other CONV3D_TILE" : "");
     }
     if (!best) {
         delete p;
@@ -351,6 +371,15 @@ conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *work
             p->ws_bytes = p->ws_queue + c3d::ps_queue_bytes();
         }
     }
+    q.gn_stats = nullptr;
+    q.gn_slots = 0;
+    q.mt_per_sample = 0;
+    if (gn_stats) {
+        q.mt_per_sample = (int32_t)((int64_t)To * Ho * Wo / c3d::kPsBM);
+        q.gn_slots = q.mt_per_sample * (c3d::kPsBM / 32);
+        p->ws_gn = (p->ws_bytes + 255) & ~(size_t)255;
+        p->ws_bytes = p->ws_gn + (size_t)d->n * (d->c_out / 8) * q.gn_slots * 16;
+    }
 
     *out = p;
     *workspace_bytes = p->ws_bytes;
@@ -398,6 +427,8 @@ conv3d_status conv3d_plan_query(conv3d_plan_t p, conv3d_plan_info *info) {
     if (p->dynamic && info->grid > kCUs) info->grid = kCUs;  // one workgroup per CU takes the units
     info->split_tiles = p->prm.sk_tiles;
     info->split_pieces = p->prm.sk_tiles ? p->prm.sk_pieces : 0;
+    info->gn_stats_slots = p->prm.gn_slots;
+    info->gn_stats_offset = p->prm.gn_slots ? p->ws_gn : 0;
     snprintf(info->kernel_name, sizeof(info->kernel_name), "conv3d_igemm_%s%s", p->tile->name,
              p->tail ? "_tail" : "");
     return ok();
@@ -445,6 +476,7 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
         q.queue = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + p->ws_queue);
         q.grid_cap = cu_count();
     }
+    if (q.gn_slots) q.gn_stats = reinterpret_cast<float4 *>(static_cast<char *>(workspace) + p->ws_gn);
     if (p->path == CONV3D_PATH_T1_FOLD) {
         _Float16 *w2 = static_cast<_Float16 *>(workspace);
         hipError_t e = c3d::launch_fold_taps(q.w, w2, p->d.c_out, p->d.kt, p->fold_khwc, p->fold_lo, p->fold_hi,
@@ -594,6 +626,54 @@ conv3d_status groupnorm_silu_bf16(const void *x, const void *gamma, const void *
                                   int64_t thw, int32_t c, int32_t groups, float eps, int32_t apply_silu,
                                   void *workspace, size_t workspace_bytes, void *stream) {
     return gn_entry(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, workspace, workspace_bytes, stream, true);
+}
+
+size_t groupnorm_silu_from_stats_workspace(int32_t n, int32_t c, int32_t groups) {
+    if (n < 1 || c < 8 || c % 8 || groups < 1 || c % groups || (c / groups) % 8 || c > 8192) return 0;
+    return c3d::gn_from_stats_workspace_bytes(n, c, groups);
+}
+
+static conv3d_status gn_stats_entry(const void *x, const void *gamma, const void *beta, void *y, int32_t n,
+                                    int64_t thw, int32_t c, int32_t groups, float eps, int32_t apply_silu,
+                                    const void *stats, int32_t stats_slots, void *workspace, size_t workspace_bytes,
+                                    void *stream, bool bf16) {
+    conv3d_status st = gn_check(x, gamma, beta, y, n, thw, c, groups, eps);
+    if (st != CONV3D_OK) return st;
+    if (!stats || misaligned(stats) || stats_slots < 1)
+        return fail(CONV3D_ERR_INVALID_ARG, "stats must be a 16-byte aligned device pointer and stats_slots >= 1");
+    if (misaligned(workspace)) return fail(CONV3D_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    const size_t need = groupnorm_silu_from_stats_workspace(n, c, groups);
+    if (!workspace || workspace_bytes < need)
+        return fail(CONV3D_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    const size_t bytes = (size_t)n * thw * c * 2, sbytes = (size_t)n * (c / 8) * stats_slots * 16;
+    if (overlap(workspace, need, x, bytes) || overlap(workspace, need, y, bytes) ||
+        overlap(workspace, need, stats, sbytes) || overlap(y, bytes, stats, sbytes))
+        return fail(CONV3D_ERR_INVALID_ARG, "workspace or stats overlaps a tensor");
+    st = check_device();
+    if (st != CONV3D_OK) return st;
+    hipError_t e = c3d::launch_groupnorm_from_stats(
+        static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(gamma), static_cast<const _Float16 *>(beta),
+        static_cast<_Float16 *>(y), n, thw, c, groups, eps, apply_silu, bf16, stats, stats_slots, workspace,
+        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CONV3D_ERR_HIP, "groupnorm launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+conv3d_status groupnorm_silu_from_stats(const void *x, const void *gamma, const void *beta, void *y, int32_t n,
+                                        int64_t thw, int32_t c, int32_t groups, float eps, int32_t apply_silu,
+                                        const void *stats, int32_t stats_slots, void *workspace,
+                                        size_t workspace_bytes, void *stream) {
+    return gn_stats_entry(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, stats, stats_slots, workspace,
+                          workspace_bytes, stream, false);
+}
+
+conv3d_status groupnorm_silu_from_stats_bf16(const void *x, const void *gamma, const void *beta, void *y,
+                                             int32_t n, int64_t thw, int32_t c, int32_t groups, float eps,
+                                             int32_t apply_silu, const void *stats, int32_t stats_slots,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+    return gn_stats_entry(x, gamma, beta, y, n, thw, c, groups, eps, apply_silu, stats, stats_slots, workspace,
+                          workspace_bytes, stream, true);
 }
 
 size_t groupnorm_silu_noalloc_max_bytes(void) { return c3d::kGnStaticScratchBytes; }

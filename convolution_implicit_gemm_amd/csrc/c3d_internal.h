@@ -36,7 +36,18 @@ struct ConvParams {
     int32_t bf16;          // elements are bf16 (else fp16)
     uint32_t *queue;       // counters of the dynamic tile schedule (workspace), or null: static
     int32_t grid_cap;      // dynamic schedule: at most this many workgroups (one per CU)
+    // GroupNorm partial statistics of y (CONV3D_F_GN_STATS), or null: float4
+    // (count, mean, M2, 0) [N][Cout/8][gn_slots] (workspace), one per
+    // (sample, 8-channel chunk, M-tile of the sample, 32-voxel row group of
+    // the tile): slot = (M-tile within the sample) * (BM/32) + row group.
+    float4 *gn_stats;
+    int32_t gn_slots;      // slots per (sample, chunk): M-tiles per sample * BM/32
+    int32_t mt_per_sample; // M-tiles per sample (voxels per sample are a multiple of BM)
 };
+
+// Output voxels per tile of the row-slab kernel (conv3d_ps.hip); its
+// GroupNorm statistics come in 32-voxel row groups.
+constexpr int kPsBM = 256;
 
 // Most K-pieces a split tile may be cut into (the fixup kernel loads them all
 // at once).
@@ -103,6 +114,13 @@ hipError_t launch_fold_taps(const _Float16 *w, _Float16 *w2, int32_t cout, int32
 
 // GroupNorm(+SiLU): workspace layout and launch.
 size_t gn_workspace_bytes(int32_t n, int64_t thw, int32_t c, int32_t groups);
+// GroupNorm(+SiLU) from the float4 partials [n][c/8][slots] a conv wrote
+// (CONV3D_F_GN_STATS); ws (gn_from_stats_workspace_bytes) holds the
+// per-channel scale and shift and the second-level partials.
+size_t gn_from_stats_workspace_bytes(int32_t n, int32_t c, int32_t groups);
+hipError_t launch_groupnorm_from_stats(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta, _Float16 *y,
+                                      int32_t n, int64_t thw, int32_t c, int32_t groups, float eps, int32_t silu,
+                                      bool bf16, const void *stats, int32_t slots, void *ws, hipStream_t s);
 hipError_t launch_groupnorm_silu(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta,
                                  _Float16 *y, int32_t n, int64_t thw, int32_t c, int32_t groups,
                                  float eps, int32_t silu, bool bf16, void *ws, hipStream_t s);

@@ -44,6 +44,7 @@
 //    waits for every outstanding load, which would drain the prefetch ring.
 //  * Workgroups are renumbered so each XCD (workgroup id mod 8) walks a
 //    contiguous range of tiles; tiles sharing input rows then share an L2.
+#include "gn_partial.h"
 #include "igemm_common.h"
 
 namespace c3d {
@@ -441,16 +442,17 @@ __global__ __launch_bounds__(256) void conv3d_fixup_kernel(ConvParams p) {
     const int mt = tile / p.n_tiles, nt = tile - mt * p.n_tiles;
     const int co = nt * BN + (wave % NWN) * WN + i * 32 + 8 * g + 4 * (lane >> 5);
     const int m = mt * BM + (wave / NWN) * WM + j * 32 + (lane & 31);
-    if (co >= p.Cout || m >= (int)p.M) return;
+    const bool ok = co < p.Cout && m < (int)p.M;
     // every load first (all pieces, bias, residual), then the sum in piece order
     const f32x4 *pp = reinterpret_cast<const f32x4 *>(p.partial) + (size_t)t * p.sk_pieces * UNITS + u;
     __builtin_assume(p.sk_pieces >= 2 && p.sk_pieces <= kMaxSplitPieces);
     f32x4 e[kMaxSplitPieces];
 #pragma unroll
-    for (int q = 0; q < kMaxSplitPieces; ++q) e[q] = q < p.sk_pieces ? pp[(size_t)q * UNITS] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = 0; q < kMaxSplitPieces; ++q)
+        e[q] = ok && q < p.sk_pieces ? pp[(size_t)q * UNITS] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const int64_t o = (int64_t)m * p.Cout + co;
-    const half4_t b4 = p.bias ? *reinterpret_cast<const half4_t *>(p.bias + co) : half4_t{};
-    const half4_t r4 = p.res ? *reinterpret_cast<const half4_t *>(p.res + o) : half4_t{};
+    const half4_t b4 = p.bias && ok ? *reinterpret_cast<const half4_t *>(p.bias + co) : half4_t{};
+    const half4_t r4 = p.res && ok ? *reinterpret_cast<const half4_t *>(p.res + o) : half4_t{};
     f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int q = 0; q < kMaxSplitPieces; ++q)
@@ -458,7 +460,31 @@ __global__ __launch_bounds__(256) void conv3d_fixup_kernel(ConvParams p) {
     half4_t h;
 #pragma unroll
     for (int c = 0; c < 4; ++c) h[c] = from_f32<E>(v[c] + to_f32<E>(b4[c]) + to_f32<E>(r4[c]));
-    *reinterpret_cast<half4_t *>(p.y + o) = h;
+    if (ok) *reinterpret_cast<half4_t *>(p.y + o) = h;
+    if (p.gn_stats) {
+        // GroupNorm partial statistics of the stored values: this wave holds
+        // one 8-channel chunk (lanes l and l + 32: its two halves) of 32
+        // voxels, one 32-voxel row group of the tile
+        float K = 0.0f, s1 = 0.0f, s2 = 0.0f, cnt = 0.0f;
+        if (ok) {
+            K = to_f32<E>(h[0]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float d = to_f32<E>(h[c]) - K;
+                s1 += d;
+                s2 = fmaf(d, d, s2);
+            }
+            cnt = 4.0f;
+        }
+        const Welford w = wave_merge(welford_from_shifted(cnt, K, s1, s2));
+        const int cbase = co - 4 * (lane >> 5);  // the chunk's first channel
+        if (lane == 0 && cbase < p.Cout) {
+            const int ns = mt / p.mt_per_sample, mtl = mt - ns * p.mt_per_sample;
+            const int rg = ((wave / NWN) * WM + j * 32) / 32;
+            p.gn_stats[((size_t)ns * (p.Cout / 8) + cbase / 8) * p.gn_slots + mtl * (BM / 32) + rg] =
+                make_float4(w.n, w.mean, w.m2, 0.0f);
+        }
+    }
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int ASTAGES, bool TAIL, typename E>

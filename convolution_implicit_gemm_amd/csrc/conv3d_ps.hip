@@ -53,6 +53,7 @@
 // x 8 tiles (ps_walk), so that the 32 tiles it runs at once share their input
 // rows in its L2; against tiles along one frame this cut the 33-frame 256x256
 // conv's time by 2.5%, mostly through a higher clock (less traffic, less power).
+#include "gn_partial.h"
 #include "igemm_common.h"
 
 namespace c3d {
@@ -60,7 +61,7 @@ namespace c3d {
 namespace {
 
 constexpr int kPsThreads = 512;
-constexpr int kPsBM = 256, kPsBN = 256, kPsBK = 64;
+constexpr int kPsBN = 256, kPsBK = 64;  // kPsBM: c3d_internal.h
 constexpr int kPsWM = 64, kPsWN = 128;
 constexpr int kPsTM = kPsWM / 32, kPsTN = kPsWN / 32;
 constexpr int kPsRB = kPsBK * 2;                  // bytes per LDS row
@@ -195,6 +196,14 @@ __device__ __forceinline__ void ps_store_tile(const ConvParams &p, const f32x16 
                 *reinterpret_cast<half4_t *>(chunk + ((rhi ^ ((v >> 4) & 1)) << 3)) = h;
             }
     ps_barrier();
+    // GroupNorm partial statistics of the stored (rounded) values, when asked
+    // for: lane l sums its chunk's 8 channels over its 16 voxels about its
+    // first value (valid voxels are a prefix in k), the lanes l and l ^ 32
+    // (the same chunk, the other voxels) merge, and lanes 0..31 write one
+    // (count, mean, M2) per (chunk, the wave's 32-voxel row group).
+    const bool stats = p.gn_stats != nullptr;
+    const bool chunk_ok = n0 + 8 * rc < p.Cout;
+    float sK = 0.0f, s1 = 0.0f, s2 = 0.0f, scnt = 0.0f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int v = row_v(k);
@@ -202,6 +211,25 @@ __device__ __forceinline__ void ps_store_tile(const ConvParams &p, const f32x16 
         if (k >= 8)  // v & 16: the halves were stored swapped
             h = __builtin_shufflevector(h, h, 4, 5, 6, 7, 0, 1, 2, 3);
         store16(ry, row_off(v, rc), h);
+        if (stats && chunk_ok && v < rows) {
+            if (k == 0) sK = to_f32<E>(h[0]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float d = to_f32<E>(h[q]) - sK;
+                s1 += d;
+                s2 = fmaf(d, d, s2);
+            }
+            scnt += 8.0f;
+        }
+    }
+    if (stats) {
+        const Welford w = lane_merge(welford_from_shifted(scnt, sK, s1, s2), 32);
+        if (lane < 32 && chunk_ok) {
+            const int mt = m0 / kPsBM;
+            const int ns = mt / p.mt_per_sample, mtl = mt - ns * p.mt_per_sample;
+            p.gn_stats[((size_t)ns * (p.Cout / 8) + (n0 / 8 + rc)) * p.gn_slots + mtl * (kPsBM / 32) + wv] =
+                make_float4(w.n, w.mean, w.m2, 0.0f);
+        }
     }
 }
 

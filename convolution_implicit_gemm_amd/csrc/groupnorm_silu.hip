@@ -30,6 +30,7 @@
 //          for every shape (a measurement switch).
 #include "c3d_internal.h"
 #include "elem16.h"
+#include "gn_partial.h"
 
 #include <cstdlib>
 #include <mutex>
@@ -117,22 +118,6 @@ size_t off_part(int32_t n, int32_t c) {
     return (b + 255) & ~(size_t)255;
 }
 
-struct Welford {
-    float n, mean, m2;
-};
-
-__device__ __forceinline__ Welford chan_merge(Welford a, Welford b) {
-    const float n = a.n + b.n;
-    if (n == 0.0f) return a;
-    const float d = b.mean - a.mean;
-    const float fb = b.n / n;
-    Welford r;
-    r.n = n;
-    r.mean = a.mean + d * fb;
-    r.m2 = a.m2 + b.m2 + d * d * a.n * fb;
-    return r;
-}
-
 template <typename E>
 __global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(const _Float16 *__restrict__ x, int64_t thw,
                                                                 int32_t c, int32_t groups, int32_t sb,
@@ -189,10 +174,7 @@ __global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(const _Float16 *_
                 cnt += 8.0f;
             }
     }
-    Welford w;
-    w.n = cnt;
-    w.mean = cnt > 0.0f ? K + s1 / cnt : 0.0f;
-    w.m2 = cnt > 0.0f ? fmaxf(s2 - s1 * (s1 / cnt), 0.0f) : 0.0f;
+    Welford w = welford_from_shifted(cnt, K, s1, s2);
     // Lanes l and l ^ off (off a multiple of a power-of-two vpv) hold the same
     // channel vector: merge them with shuffles first, so that only one entry
     // per (wave, vector) goes through LDS.
@@ -430,18 +412,14 @@ __global__ __launch_bounds__(kMaxThreads) void gn_apply_merge_kernel(
     apply_stream<SILU, E>(xs, ys, thw, vpv, vi, v, vox_step, a, bsh, h, loaded);
 }
 
+// The apply pass over the partials `part` ([N][G][g.sb]): the merged apply
+// where they fit one block's merge (unless CONV3D_GN_FINAL=1, a measurement
+// switch), else the final kernel (scales and shifts to the workspace) and the
+// plain apply.
 template <typename E>
-hipError_t launch_gn(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta, _Float16 *y, int32_t n,
-                     int64_t thw, int32_t c, int32_t groups, float eps, int32_t silu, void *ws, hipStream_t s) {
-    const GnGeom g = gn_geom(n, thw, c, groups);
-    char *base = static_cast<char *>(ws);
-    float *scale = reinterpret_cast<float *>(base);
-    float *shift = scale + (size_t)n * c;
-    float4 *part = reinterpret_cast<float4 *>(base + off_part(n, c));
-    hipLaunchKernelGGL(gn_stats_kernel<E>, dim3(g.sb, n), dim3(g.sthreads), 0, s, x, thw, c, groups, g.sb, part);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // CONV3D_GN_FINAL=1 keeps the separate final kernel (for measurements)
+hipError_t launch_apply(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta, _Float16 *y, int32_t n,
+                        int64_t thw, int32_t c, int32_t groups, float eps, int32_t silu, const GnGeom &g,
+                        const float4 *part, void *ws, hipStream_t s) {
     const char *fin = getenv("CONV3D_GN_FINAL");
     if (g.merged && !(fin && *fin == '1')) {
         if (silu)
@@ -452,9 +430,11 @@ hipError_t launch_gn(const _Float16 *x, const _Float16 *gamma, const _Float16 *b
                                c, groups, g.sb, g.tpg, part, eps, gamma, beta);
         return hipGetLastError();
     }
+    float *scale = static_cast<float *>(ws);
+    float *shift = scale + (size_t)n * c;
     hipLaunchKernelGGL(gn_final_kernel<E>, dim3(groups, n), dim3(kFinalThreads), 0, s, part, g.sb, c, groups, eps,
                        gamma, beta, scale, shift);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (silu)
         hipLaunchKernelGGL((gn_apply_kernel<true, E>), dim3(g.ab, n), dim3(g.athreads), 0, s, x, y, thw, c, scale,
@@ -463,6 +443,73 @@ hipError_t launch_gn(const _Float16 *x, const _Float16 *gamma, const _Float16 *b
         hipLaunchKernelGGL((gn_apply_kernel<false, E>), dim3(g.ab, n), dim3(g.athreads), 0, s, x, y, thw, c, scale,
                            shift);
     return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_gn(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta, _Float16 *y, int32_t n,
+                     int64_t thw, int32_t c, int32_t groups, float eps, int32_t silu, void *ws, hipStream_t s) {
+    const GnGeom g = gn_geom(n, thw, c, groups);
+    float4 *part = reinterpret_cast<float4 *>(static_cast<char *>(ws) + off_part(n, c));
+    hipLaunchKernelGGL(gn_stats_kernel<E>, dim3(g.sb, n), dim3(g.sthreads), 0, s, x, thw, c, groups, g.sb, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_apply<E>(x, gamma, beta, y, n, thw, c, groups, eps, silu, g, part, ws, s);
+}
+
+// First level of the merge of many partials: block (r, g, n) merges the
+// partials [r*sb/R, (r+1)*sb/R) of group g of sample n (eight loads in flight
+// per thread, then shuffles and LDS) into out[(n*G + g)*R + r].
+constexpr int kReduceThreads = 256;
+
+__global__ __launch_bounds__(kReduceThreads) void gn_reduce_kernel(const float4 *__restrict__ part, int32_t sb,
+                                                                  int32_t groups, float4 *__restrict__ out) {
+    __shared__ float4 red[kReduceThreads / 64];
+    const int r = blockIdx.x, g = blockIdx.y, n = blockIdx.z, R = gridDim.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float4 *p = part + ((size_t)n * groups + g) * sb;
+    const int b0 = (int)((int64_t)sb * r / R), b1 = (int)((int64_t)sb * (r + 1) / R);
+    Welford acc = {0.0f, 0.0f, 0.0f};
+    int b = b0 + tid;
+    for (; b + 7 * kReduceThreads < b1; b += 8 * kReduceThreads) {
+        float4 e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) e[u] = p[b + u * kReduceThreads];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc = chan_merge(acc, Welford{e[u].x, e[u].y, e[u].z});
+    }
+    for (; b < b1; b += kReduceThreads) {
+        const float4 e = p[b];
+        acc = chan_merge(acc, Welford{e.x, e.y, e.z});
+    }
+    acc = wave_merge(acc);
+    if (lane == 0) red[wave] = make_float4(acc.n, acc.mean, acc.m2, 0.0f);
+    __syncthreads();
+    if (tid == 0) {
+        Welford t = {0.0f, 0.0f, 0.0f};
+        for (int w = 0; w < kReduceThreads / 64; ++w) t = chan_merge(t, Welford{red[w].x, red[w].y, red[w].z});
+        out[((size_t)n * groups + g) * R + r] = make_float4(t.n, t.mean, t.m2, 0.0f);
+    }
+}
+
+// Second-level partials per (sample, group) of the from-statistics path.
+constexpr int kFromStatsR = 16;
+
+template <typename E>
+hipError_t launch_gn_from_stats(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta, _Float16 *y,
+                                int32_t n, int64_t thw, int32_t c, int32_t groups, float eps, int32_t silu,
+                                const float4 *stats, int32_t slots, void *ws, hipStream_t s) {
+    // [n][c/8][slots]: a group's (c/groups/8) chunks of partials are one run
+    const int32_t sb = (c / groups / 8) * slots;
+    // workspace: scale/shift [n][c] x2 floats, then the second-level partials [n][G][R]
+    float4 *part2 = reinterpret_cast<float4 *>(static_cast<char *>(ws) + off_part(n, c));
+    const int R = sb < kFromStatsR ? sb : kFromStatsR;
+    hipLaunchKernelGGL(gn_reduce_kernel, dim3(R, groups, n), dim3(kReduceThreads), 0, s, stats, sb, groups, part2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    GnGeom g = gn_geom(n, thw, c, groups);
+    g.sb = R;
+    g.merged = g.tpg > 0 && (size_t)groups * R * sizeof(float4) <= kMaxMergeBytes;
+    return launch_apply<E>(x, gamma, beta, y, n, thw, c, groups, eps, silu, g, part2, ws, s);
 }
 
 constexpr int kMaxScratchDevices = 64;
@@ -488,9 +535,21 @@ hipError_t gn_static_scratch(void **ptr) {
     return hipSuccess;
 }
 
+size_t gn_from_stats_workspace_bytes(int32_t n, int32_t c, int32_t groups) {
+    return off_part(n, c) + (size_t)n * groups * kFromStatsR * sizeof(float4);
+}
+
 size_t gn_workspace_bytes(int32_t n, int64_t thw, int32_t c, int32_t groups) {
     const GnGeom g = gn_geom(n, thw, c, groups);
     return off_part(n, c) + (size_t)n * g.sb * groups * sizeof(float4);
+}
+
+hipError_t launch_groupnorm_from_stats(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta, _Float16 *y,
+                                      int32_t n, int64_t thw, int32_t c, int32_t groups, float eps, int32_t silu,
+                                      bool bf16, const void *stats, int32_t slots, void *ws, hipStream_t s) {
+    const float4 *st = static_cast<const float4 *>(stats);
+    if (bf16) return launch_gn_from_stats<__bf16>(x, gamma, beta, y, n, thw, c, groups, eps, silu, st, slots, ws, s);
+    return launch_gn_from_stats<_Float16>(x, gamma, beta, y, n, thw, c, groups, eps, silu, st, slots, ws, s);
 }
 
 hipError_t launch_groupnorm_silu(const _Float16 *x, const _Float16 *gamma, const _Float16 *beta, _Float16 *y,

@@ -60,7 +60,8 @@ enum {
     CONV3D_F_RESIDUAL = 2u,        /* add residual[N,To,Ho,Wo,Cout] (fp32 add, one rounding) */
     CONV3D_F_NO_T1_FASTPATH = 4u,  /* never fold temporal taps, even when it is exact */
     CONV3D_F_BF16 = 8u,            /* x, weight, bias, residual and y are bf16, not fp16 */
-    CONV3D_F_CHUNK = 16u           /* chunked causal decoding: see conv3d_forward_chunk */
+    CONV3D_F_CHUNK = 16u,          /* chunked causal decoding: see conv3d_forward_chunk */
+    CONV3D_F_GN_STATS = 32u        /* also write GroupNorm partial statistics of y: see below */
 };
 
 /* Execution paths a plan may choose. */
@@ -108,6 +109,8 @@ typedef struct {
     char kernel_name[64];         /* the main kernel's symbol stem */
     int32_t split_tiles;          /* tiles whose K range is split over several workgroups */
     int32_t split_pieces;         /* K-pieces per split tile (0 if none) */
+    int32_t gn_stats_slots;       /* CONV3D_F_GN_STATS: partials per (sample, 8-channel chunk); else 0 */
+    size_t gn_stats_offset;       /* CONV3D_F_GN_STATS: their byte offset in the workspace; else 0 */
 } conv3d_plan_info;
 
 /*
@@ -134,6 +137,20 @@ typedef struct {
  * CONV3D_TILE=<name> forces a tile configuration; CONV3D_STREAMK=0 forbids and
  * =1 forces the K split; CONV3D_DYNAMIC=0 forbids and =1 forces the
  * one-workgroup-per-CU schedule where the row-slab tile is used.
+ * CONV3D_F_GN_STATS (the producing half of a GroupNorm fused into the conv
+ * that feeds it, after the A1111 Metal fork write-up's fused GroupNorm+SiLU,
+ * news.bugfactory.tech item 4286): conv3d_forward also writes, into the
+ * workspace at info.gn_stats_offset, float4 partials (count, mean, M2, 0) of
+ * the values it stores in y, laid out [n][c_out/8][info.gn_stats_slots]: one
+ * per (sample, 8-channel chunk, 32 consecutive output voxels of the sample),
+ * each over those 8 x 32 values (fewer where c_out or the sample ends).  Every
+ * slot is written on every call.  groupnorm_silu_from_stats then normalises y
+ * without reading it for statistics.  The plan must run the general path on
+ * the row-slab tile, so CONV3D_F_GN_STATS is UNSUPPORTED for a T = 1 fold
+ * (pass CONV3D_F_NO_T1_FASTPATH as well), a 1x1x1 conv, shapes the row-slab
+ * tile does not cover (kw = 3 with pad_w = 1, kt and kh at most 3, output
+ * rows a multiple of 32 voxels and w_out = w), and t_out*h_out*w_out not a
+ * multiple of 256; INVALID_ARG with CONV3D_F_CHUNK.
  */
 conv3d_status conv3d_plan(const conv3d_desc *d, conv3d_plan_t *out, size_t *workspace_bytes);
 
@@ -183,6 +200,32 @@ conv3d_status conv3d_forward(conv3d_plan_t p, const void *x, const void *weight,
 conv3d_status conv3d_forward_chunk(conv3d_plan_t p, const void *x_prev, const void *x, const void *weight,
                                    const void *bias, const void *residual, void *y, void *workspace,
                                    size_t workspace_bytes, void *stream);
+
+/*
+ * GroupNorm + optional SiLU whose statistics were produced by the conv that
+ * wrote x (a plan with CONV3D_F_GN_STATS): the same operation and rounding
+ * as groupnorm_silu, with each group's mean and variance merged (Chan's
+ * pairwise update, in fp32) from `stats`, the float4 partials
+ * [n][c/8][stats_slots] that conv3d_forward left at info.gn_stats_offset of
+ * its workspace (stats_slots = info.gn_stats_slots), instead of a pass over x.
+ * x must be that conv's y, unchanged.  The workspace (at least
+ * groupnorm_silu_from_stats_workspace(n, c, groups) bytes) is scratch.  Two
+ * launches: a first merge of each group's partials into 16 by many blocks,
+ * then the apply pass, whose blocks finish the merge themselves.  Errors as
+ * groupnorm_silu, plus INVALID_ARG for a null or misaligned stats or
+ * stats_slots < 1.  groupnorm_silu_from_stats_workspace returns 0 for
+ * arguments groupnorm_silu_from_stats would reject.
+ */
+size_t groupnorm_silu_from_stats_workspace(int32_t n, int32_t c, int32_t groups);
+conv3d_status groupnorm_silu_from_stats(const void *x, const void *gamma, const void *beta, void *y,
+                                        int32_t n, int64_t thw, int32_t c, int32_t groups, float eps,
+                                        int32_t apply_silu, const void *stats, int32_t stats_slots,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+/* The same for bf16 x, gamma, beta and y (a plan with CONV3D_F_BF16). */
+conv3d_status groupnorm_silu_from_stats_bf16(const void *x, const void *gamma, const void *beta, void *y,
+                                             int32_t n, int64_t thw, int32_t c, int32_t groups, float eps,
+                                             int32_t apply_silu, const void *stats, int32_t stats_slots,
+                                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * GroupNorm + optional SiLU over channels-last fp16 data.

@@ -238,6 +238,58 @@ def test_groupnorm_argument_checks():
     assert gn(wsb=8) == c3d.CONV3D_ERR_WORKSPACE
 
 
+def test_gn_stats_plans_and_layout():
+    f = c3d.CONV3D_F_BIAS | c3d.CONV3D_F_GN_STATS
+    # the block conv: 17 x 128 x 128 voxels, 1088 row-slab tiles, 8 row groups each
+    p = c3d.conv3d_plan(desc(t=17, h=128, w=128, c_in=256, c_out=256, flags=f))
+    info = p.info()
+    assert info.tile_m == 256 and info.tile_n == 256 and b"ps" in info.kernel_name
+    assert info.gn_stats_slots == 17 * 128 * 128 // 32
+    assert info.gn_stats_offset % 256 == 0 and info.gn_stats_offset > 0
+    assert p.workspace_bytes == info.gn_stats_offset + 1 * (256 // 8) * info.gn_stats_slots * 16
+    # without the flag: no statistics, a smaller workspace, the same tile
+    q = c3d.conv3d_plan(desc(t=17, h=128, w=128, c_in=256, c_out=256))
+    assert q.info().gn_stats_slots == 0 and q.info().gn_stats_offset == 0
+    assert q.workspace_bytes < p.workspace_bytes and q.info().kernel_name == info.kernel_name
+    # two samples, 512 -> 128 channels: [n][c_out/8][slots]
+    p2 = c3d.conv3d_plan(desc(n=2, t=4, h=32, w=64, c_in=512, c_out=128, flags=f))
+    i2 = p2.info()
+    assert i2.gn_stats_slots == 4 * 32 * 64 // 32
+    assert p2.workspace_bytes == i2.gn_stats_offset + 2 * 16 * i2.gn_stats_slots * 16
+    # the T=1 fold and the 1x1x1 stream do not produce statistics
+    assert plan_status(desc(t=1, flags=f)) == c3d.CONV3D_ERR_UNSUPPORTED
+    assert plan_status(desc(t=1, flags=f | c3d.CONV3D_F_NO_T1_FASTPATH)) == c3d.CONV3D_OK
+    assert plan_status(desc(kt=1, kh=1, kw=1, pad_t_front=0, pad_h=0, pad_w=0, flags=f)) == \
+        c3d.CONV3D_ERR_UNSUPPORTED
+    # shapes outside the row-slab tile, or samples that do not fill whole tiles
+    assert plan_status(desc(w=48, flags=f)) == c3d.CONV3D_ERR_UNSUPPORTED
+    assert plan_status(desc(kh=5, pad_h=2, flags=f)) == c3d.CONV3D_ERR_UNSUPPORTED
+    assert plan_status(desc(t=3, h=3, w=32, flags=f)) == c3d.CONV3D_ERR_UNSUPPORTED   # 288 voxels
+    assert plan_status(desc(flags=f | c3d.CONV3D_F_CHUNK)) == c3d.CONV3D_ERR_INVALID_ARG
+
+
+def test_groupnorm_from_stats_argument_checks():
+    lib = c3d.load_library()
+    # per-channel scale and shift (256-byte aligned), then 16 second-level partials per (sample, group)
+    assert c3d.groupnorm_silu_from_stats_workspace(2, 256, 32) == 2 * 256 * 8 + 2 * 32 * 16 * 16
+    assert c3d.groupnorm_silu_from_stats_workspace(0, 256, 32) == 0
+    assert c3d.groupnorm_silu_from_stats_workspace(1, 12, 1) == 0
+    assert c3d.groupnorm_silu_from_stats_workspace(1, 96, 32) == 0   # 3 channels per group
+
+    def gn(x=A, y=A + 512 * MB, n=1, thw=100, c=256, g=32, eps=1e-6, st=A + 1700 * MB, slots=4,
+           ws=A + 1024 * MB, wsb=1 << 20, bf16=False):
+        fn = lib.groupnorm_silu_from_stats_bf16 if bf16 else lib.groupnorm_silu_from_stats
+        return fn(x, A + 1536 * MB, A + 1600 * MB, y, n, thw, c, g, eps, 1, st, slots, ws, wsb, None)
+    assert gn(x=None) == c3d.CONV3D_ERR_INVALID_ARG
+    assert gn(g=3) == c3d.CONV3D_ERR_INVALID_ARG
+    assert gn(c=96) == c3d.CONV3D_ERR_UNSUPPORTED
+    assert gn(st=None) == c3d.CONV3D_ERR_INVALID_ARG
+    assert gn(st=A + 1700 * MB + 8) == c3d.CONV3D_ERR_INVALID_ARG
+    assert gn(slots=0, bf16=True) == c3d.CONV3D_ERR_INVALID_ARG
+    assert gn(wsb=8) == c3d.CONV3D_ERR_WORKSPACE
+    assert gn(st=A + 1024 * MB) == c3d.CONV3D_ERR_INVALID_ARG     # stats overlap the workspace
+
+
 def test_groupnorm_noalloc_argument_checks_and_limit():
     lib = c3d.load_library()
     assert c3d.groupnorm_silu_noalloc_max_bytes() == 4 << 20
@@ -331,7 +383,7 @@ def test_bf16_flag_plans_every_path():
               desc(kt=1, kh=1, kw=1, pad_t_front=0, pad_h=0, pad_w=0, flags=c3d.CONV3D_F_BF16)):
         p = c3d.conv3d_plan(d)
         assert p.info().flops > 0
-    assert plan_status(desc(flags=32)) == c3d.CONV3D_ERR_INVALID_ARG
+    assert plan_status(desc(flags=64)) == c3d.CONV3D_ERR_INVALID_ARG
 
 
 def test_chunk_plans_and_argument_checks():
