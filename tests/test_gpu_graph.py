@@ -148,3 +148,47 @@ def test_dynamic_tile_schedule_graph_replays_equal_eager():
         c3d.conv3d_forward(plan, x, w, b, None, y_eager, ws_eager)
         torch.cuda.synchronize()
         assert torch.equal(bits(y), bits(y_eager)), k
+
+
+class StatsBlockBuffers(BlockBuffers):
+    """The block with GN2 from conv1's statistics (conv1 planned with CONV3D_F_GN_STATS)."""
+
+    def __init__(self, s, p1, p2, params, groups=32):
+        super().__init__(s, p1, p2, params, groups)
+        self.stats, self.slots = c3d.gn_stats_view(p1, self.ws1)
+        self.sws = torch.empty(c3d.groupnorm_silu_from_stats_workspace(s.n, s.cout, groups), dtype=torch.uint8,
+                               device="cuda:0")
+
+    def run(self):
+        s, p = self.s, self.p
+        c3d.groupnorm_silu(self.x, p["gamma1"], p["beta1"], self.a1, s.n, self.thw, s.cin, self.groups, 1e-6,
+                           True, self.gws)
+        c3d.conv3d_forward(self.p1, self.a1, p["w1"], p["b1"], None, self.c1, self.ws1)
+        c3d.groupnorm_silu_from_stats(self.c1, p["gamma2"], p["beta2"], self.a2, s.n, self.thw, s.cout,
+                                      self.groups, 1e-6, True, self.stats, self.slots, self.sws)
+        c3d.conv3d_forward(self.p2, self.a2, p["w2"], p["b2"], self.x, self.out, self.ws2)
+
+
+@pytest.mark.parametrize("dynamic", ["0", "1"])
+def test_block_with_gn2_from_conv1_statistics_graph_replays_equal_eager(dynamic):
+    # conv1 with statistics, forced onto a K split (the fixup's partials too),
+    # on the static or the one-workgroup-per-CU schedule (its counter-clearing kernel)
+    s = ConvShape(1, 4, 16, 64, 256, 256)
+    with env_var("CONV3D_STREAMK", "1"), env_var("CONV3D_DYNAMIC", dynamic):
+        p1 = c3d.conv3d_plan(conv_desc(s, c3d.CONV3D_F_BIAS | c3d.CONV3D_F_GN_STATS))
+    assert p1.info().split_tiles > 0 and p1.info().gn_stats_slots > 0
+    p2 = c3d.conv3d_plan(conv_desc(s, c3d.CONV3D_F_BIAS | c3d.CONV3D_F_RESIDUAL))
+    d = workloads.block_inputs(s, 1550)
+    params = {k: dev(d[k]) for k in ("gamma1", "beta1", "w1", "b1", "gamma2", "beta2", "w2", "b2")}
+    graphed, eager = StatsBlockBuffers(s, p1, p2, params), StatsBlockBuffers(s, p1, p2, params)
+    graphed.x.copy_(dev(d["x"]))
+    g = capture(graphed.run)
+    for k in range(REPLAYS):
+        xk = dev(workloads.normal_f16(np.random.SeedSequence(1560 + k), s.x_shape))
+        graphed.x.copy_(xk)
+        g.replay()
+        eager.x.copy_(xk)
+        eager.run()
+        torch.cuda.synchronize()
+        for name in ("a1", "c1", "a2", "out"):
+            assert torch.equal(bits(getattr(graphed, name)), bits(getattr(eager, name))), (k, name)
