@@ -641,6 +641,9 @@ static conv3d_status gn_stats_entry(const void *x, const void *gamma, const void
     if (st != CONV3D_OK) return st;
     if (!stats || misaligned(stats) || stats_slots < 1)
         return fail(CONV3D_ERR_INVALID_ARG, "stats must be a 16-byte aligned device pointer and stats_slots >= 1");
+    if ((int64_t)stats_slots * 32 != thw)
+        return fail(CONV3D_ERR_INVALID_ARG, "stats_slots (%d) must be thw / 32 (thw %lld): one partial per 32 voxels",
+                    stats_slots, (long long)thw);
     if (misaligned(workspace)) return fail(CONV3D_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     const size_t need = groupnorm_silu_from_stats_workspace(n, c, groups);
     if (!workspace || workspace_bytes < need)

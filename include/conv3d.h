@@ -213,8 +213,9 @@ conv3d_status conv3d_forward_chunk(conv3d_plan_t p, const void *x_prev, const vo
  * launches: a first merge of each group's partials into 16 by many blocks,
  * then the apply pass, whose blocks finish the merge themselves.  Errors as
  * groupnorm_silu, plus INVALID_ARG for a null or misaligned stats or
- * stats_slots < 1.  groupnorm_silu_from_stats_workspace returns 0 for
- * arguments groupnorm_silu_from_stats would reject.
+ * stats_slots other than thw / 32 (one partial per 32 voxels of a sample).
+ * groupnorm_silu_from_stats_workspace returns 0 for arguments
+ * groupnorm_silu_from_stats would reject.
  */
 size_t groupnorm_silu_from_stats_workspace(int32_t n, int32_t c, int32_t groups);
 conv3d_status groupnorm_silu_from_stats(const void *x, const void *gamma, const void *beta, void *y,

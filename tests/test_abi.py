@@ -276,7 +276,7 @@ def test_groupnorm_from_stats_argument_checks():
     assert c3d.groupnorm_silu_from_stats_workspace(1, 12, 1) == 0
     assert c3d.groupnorm_silu_from_stats_workspace(1, 96, 32) == 0   # 3 channels per group
 
-    def gn(x=A, y=A + 512 * MB, n=1, thw=100, c=256, g=32, eps=1e-6, st=A + 1700 * MB, slots=4,
+    def gn(x=A, y=A + 512 * MB, n=1, thw=128, c=256, g=32, eps=1e-6, st=A + 1700 * MB, slots=4,
            ws=A + 1024 * MB, wsb=1 << 20, bf16=False):
         fn = lib.groupnorm_silu_from_stats_bf16 if bf16 else lib.groupnorm_silu_from_stats
         return fn(x, A + 1536 * MB, A + 1600 * MB, y, n, thw, c, g, eps, 1, st, slots, ws, wsb, None)
@@ -286,6 +286,8 @@ def test_groupnorm_from_stats_argument_checks():
     assert gn(st=None) == c3d.CONV3D_ERR_INVALID_ARG
     assert gn(st=A + 1700 * MB + 8) == c3d.CONV3D_ERR_INVALID_ARG
     assert gn(slots=0, bf16=True) == c3d.CONV3D_ERR_INVALID_ARG
+    assert gn(slots=5) == c3d.CONV3D_ERR_INVALID_ARG                # thw / 32 = 4 partials per chunk
+    assert "thw / 32" in c3d.conv3d_last_error()
     assert gn(wsb=8) == c3d.CONV3D_ERR_WORKSPACE
     assert gn(st=A + 1024 * MB) == c3d.CONV3D_ERR_INVALID_ARG     # stats overlap the workspace
 
