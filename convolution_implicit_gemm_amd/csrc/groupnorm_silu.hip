@@ -5,14 +5,14 @@
 // passes are HBM-bound streams, so the design is about coalescing, not math:
 //
 //  stats:  grid (SB, N).  Every thread reads 16-byte vectors (8 channels of
-//          one group) of consecutive voxels, so a block reads one contiguous
-//          range.  The thread count is a multiple of C/8, so each thread keeps
-//          one group and accumulates in registers with the shifted-data
-//          method (sums of x-K and (x-K)^2 about its first value K, fp32;
-//          eight 16-byte loads in flight, left in the MALL for the apply
-//          pass),
-//          then the block merges threads of a group (Chan's pairwise
-//          update) and writes (count, mean, M2) partials.
+//          one group); a block reads whole voxels, block-sized slices
+//          b, b + SB, b + 2 SB, ... of the sample.  The thread count is a
+//          multiple of C/8, so each thread keeps one group and accumulates
+//          in registers with the shifted-data method (sums of x-K and
+//          (x-K)^2 about its first value K, fp32; eight 16-byte loads in
+//          flight, left in the MALL for the apply pass); then the block
+//          merges the threads of a group (Chan's pairwise update) and writes
+//          (count, mean, M2) partials.
 //  apply:  grid (MB, N) of persistent blocks (256 over all samples).  Every
 //          block first merges each group's SB partials (one contiguous run
 //          per group, a power-of-two team of threads per group, then
@@ -130,8 +130,11 @@ __global__ __launch_bounds__(kMaxThreads) void gn_stats_kernel(const _Float16 *_
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
     const int vi = tid % vpv;
-    const int vox_step = nthr / vpv;
-    const int64_t v_begin = thw * b / sb, v_end = thw * (b + 1) / sb;
+    // Block b reads the block-sized slices b, b + sb, b + 2 sb, ... of the
+    // sample (any partition gives valid partials).  Contiguous per-block
+    // ranges, read in lockstep at one fixed stride, measured slower.
+    const int64_t vox_step = (int64_t)(nthr / vpv) * sb;
+    const int64_t v_begin = (int64_t)b * (nthr / vpv), v_end = thw;
     const half8_t *xs = reinterpret_cast<const half8_t *>(x + (size_t)n * thw * c);
 
     // shifted-data accumulation about the first value K this thread reads.
