@@ -31,10 +31,10 @@ def f64(a):
     return oracle.bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
 
 
-def conv_with_stats(shape, d, res=None, split=None, dynamic=None, bf16=False):
-    """(y with the flag, y without it, device y, plan, workspace) for one conv."""
+def conv_with_stats(shape, d, res=None, split=None, dynamic=None, bf16=False, extra_flags=0):
+    """(y with the flag, y without it, plan, workspace) for one conv."""
     flags = c3d.CONV3D_F_BIAS | (c3d.CONV3D_F_RESIDUAL if res is not None else 0) | \
-        (c3d.CONV3D_F_BF16 if bf16 else 0)
+        (c3d.CONV3D_F_BF16 if bf16 else 0) | extra_flags
     dt = torch.bfloat16 if bf16 else torch.float16
     out = []
     for extra in (c3d.CONV3D_F_GN_STATS, 0):
@@ -67,7 +67,7 @@ def gn_from_stats(y, plan, ws, n, thw, c, groups, gamma, beta, silu=True, bf16=F
     return out
 
 
-CASES = [  # (shape, groups, residual, split, dynamic, dtype)
+CASES = [  # (shape, groups, residual, split, dynamic, dtype[, extra flags])
     (ConvShape(1, 2, 16, 32, 64, 256), 32, False, "0", "0", "f16"),     # whole tiles, static schedule
     (ConvShape(1, 2, 16, 32, 64, 256), 32, False, "1", "0", "f16"),     # every tile split: the fixup's statistics
     (ConvShape(1, 4, 16, 64, 64, 256), 32, True, None, "1", "f16"),     # one workgroup per CU, a residual
@@ -75,17 +75,20 @@ CASES = [  # (shape, groups, residual, split, dynamic, dtype)
     (ConvShape(1, 2, 8, 64, 72, 384), 24, True, "1", "0", "f16"),       # Cin tail, 1.5 channel tiles, split
     (ConvShape(1, 2, 32, 32, 64, 512), 16, False, "0", "1", "f16"),     # 32-channel groups (4 chunks each)
     (ConvShape(1, 2, 16, 32, 64, 256), 32, True, None, None, "bf16"),   # bf16
+    # one frame through the general path (the T=1 fold writes no statistics)
+    (ConvShape(1, 1, 16, 32, 64, 256), 32, False, None, None, "f16", c3d.CONV3D_F_NO_T1_FASTPATH),
 ]
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_conv_gn_stats_small(case):
-    s, groups, with_res, split, dynamic, dtype = CASES[case]
+    s, groups, with_res, split, dynamic, dtype = CASES[case][:6]
+    extra = CASES[case][6] if len(CASES[case]) > 6 else 0
     bf16 = dtype == "bf16"
     d = workloads.conv_inputs(s, 1500 + case, dtype=dtype)
     od = out_dims(s)
     res = workloads.normal_f16(np.random.SeedSequence(1600 + case), od, dtype=dtype) if with_res else None
-    ys, yp, plan, ws = conv_with_stats(s, d, res, split, dynamic, bf16)
+    ys, yp, plan, ws = conv_with_stats(s, d, res, split, dynamic, bf16, extra)
     assert torch.equal(ys.view(torch.int16), yp.view(torch.int16)), "the statistics changed y"
     g = workloads.gn_inputs(1, (1, 1, 1), s.cout, 1700 + case, dtype=dtype)
     n, thw = s.n, od[1] * od[2] * od[3]
